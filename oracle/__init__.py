@@ -1,0 +1,136 @@
+"""CPU oracle for diagonal-aware sparse decode attention (fp64).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the GPU library.  The algorithm itself lives in ``dsa_oracle.c`` (Algorithm 1
+of "Understanding and Exploiting Diagonal Attention Sparsity in Autoregressive
+Image Generation", Section 4); this module compiles it with gcc and marshals
+numpy arrays.
+
+Every function here is pinned by ``tests/test_oracle_*.py``; none is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "_liboracle.so")
+
+_P = ctypes.c_void_p
+
+
+def build() -> str:
+    """Compile dsa_oracle.c into _liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_dsa_lane.restype = ctypes.c_int
+        lib.oracle_dsa_lane.argtypes = [ctypes.c_int] * 6 + [_P] * 13
+        lib.oracle_dense_lane.restype = ctypes.c_int
+        lib.oracle_dense_lane.argtypes = [ctypes.c_int] * 3 + [_P] * 6
+        _lib = lib
+    return _lib
+
+
+def widen(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact fp64 copy of generator output: uint16 bf16 bit patterns (dtype 1) or float32 (dtype 0)."""
+    if dtype == 1:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_P)
+
+
+def _f64(a, shape):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if a.shape != shape:
+        raise ValueError("expected shape %s, got %s" % (shape, a.shape))
+    return a
+
+
+def run_lane(L_p, N_r, N_att, sink, q, kp, vp, k, v, follow=None, masks=False, gaps=False):
+    """Algorithm 1 on one lane for T = len(q) decode steps.
+
+    q, k, v: [T][d] (k, v indexed by decode position); kp, vp: [L_p][d]; all fp64.
+    follow: optional int array [T]: at selection steps append follow[t] to the
+    skip set instead of the oracle's own argmin (it must be a candidate).
+    Returns a dict with out [T][d], choice [T], evicted [T], n_dec [T] and,
+    on request, gap [T], att_mask [T][T] and skip_mask [T][T].
+    """
+    T, d = np.shape(q)
+    q = _f64(q, (T, d))
+    k = _f64(k, (T, d))
+    v = _f64(v, (T, d))
+    kp = _f64(kp, (L_p, d))
+    vp = _f64(vp, (L_p, d))
+    out = np.empty((T, d), np.float64)
+    choice = np.empty(T, np.int32)
+    evicted = np.empty(T, np.int32)
+    n_dec = np.empty(T, np.int32)
+    fol = None if follow is None else np.ascontiguousarray(follow, dtype=np.int32)
+    gap = np.zeros(T, np.float64) if (gaps or follow is not None) else None
+    att = np.zeros((T, T), np.uint8) if masks else None
+    skp = np.zeros((T, T), np.uint8) if masks else None
+    rc = _load().oracle_dsa_lane(L_p, N_r, N_att, sink, d, T, _ptr(q), _ptr(kp), _ptr(vp), _ptr(k), _ptr(v),
+                                 _ptr(fol), _ptr(out), _ptr(choice), _ptr(evicted), _ptr(n_dec), _ptr(gap),
+                                 _ptr(att), _ptr(skp))
+    if rc == -2:
+        raise ValueError("follow names a position that is not a candidate")
+    if rc != 0:
+        raise ValueError("oracle_dsa_lane failed (%d)" % rc)
+    res = {"out": out, "choice": choice, "evicted": evicted, "n_dec": n_dec}
+    if gap is not None:
+        res["gap"] = gap
+    if masks:
+        res["att_mask"] = att.astype(bool)
+        res["skip_mask"] = skp.astype(bool)
+    return res
+
+
+def run_dense_lane(L_p, q, kp, vp, k, v):
+    """Dense decode attention: step t attends all prompt rows and decode positions 0..t."""
+    T, d = np.shape(q)
+    q = _f64(q, (T, d))
+    k = _f64(k, (T, d))
+    v = _f64(v, (T, d))
+    kp = _f64(kp, (L_p, d))
+    vp = _f64(vp, (L_p, d))
+    out = np.empty((T, d), np.float64)
+    rc = _load().oracle_dense_lane(L_p, d, T, _ptr(q), _ptr(kp), _ptr(vp), _ptr(k), _ptr(v), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_dense_lane failed (%d)" % rc)
+    return out
+
+
+def lane_inputs(workload, layer, b, h, T=None):
+    """fp64 inputs of one lane from the shared seeded generator: (q, kp, vp, k, v)."""
+    import synth
+
+    T = workload.L_dec if T is None else T
+    dt = workload.dtype
+    q = widen(workload.lane(layer, b, h, synth.Q, 0, T), dt)
+    k = widen(workload.lane(layer, b, h, synth.K, 0, T), dt)
+    v = widen(workload.lane(layer, b, h, synth.V, 0, T), dt)
+    kp = widen(workload.lane(layer, b, h, synth.KP), dt)
+    vp = widen(workload.lane(layer, b, h, synth.VP), dt)
+    return q, kp, vp, k, v
