@@ -1,0 +1,20 @@
+"""Diagonal-aware sparse decode attention on AMD MI355X (gfx950).
+
+Python binding of ``libdsa.so`` (C ABI in ``include/dsa.h``): the functions
+carry the C names and only marshal arguments.  Every step of the decode runs
+in the HIP kernels; there is no fallback of any kind, and loading fails loudly
+when the library has not been built (``python -m
+autoregressive_image_generation_amd._build``).
+"""
+from .binding import (DSA_BF16, DSA_F32, DsaError, State, dense_append_kv, dense_append_prompt, dense_decode_step,
+                      dense_state_init, dense_state_workspace_bytes, dsa_append_kv, dsa_append_prompt,
+                      dsa_decode_step, dsa_last_error, dsa_read_state, dsa_set_stream, dsa_set_waves,
+                      dsa_state_destroy, dsa_state_init, dsa_state_step, dsa_state_workspace_bytes, dsa_strerror,
+                      exported_symbols, library, library_path)
+
+__all__ = [
+    "DSA_BF16", "DSA_F32", "DsaError", "State", "dense_append_kv", "dense_append_prompt", "dense_decode_step",
+    "dense_state_init", "dense_state_workspace_bytes", "dsa_append_kv", "dsa_append_prompt", "dsa_decode_step",
+    "dsa_last_error", "dsa_read_state", "dsa_set_stream", "dsa_set_waves", "dsa_state_destroy", "dsa_state_init",
+    "dsa_state_step", "dsa_state_workspace_bytes", "dsa_strerror", "exported_symbols", "library", "library_path",
+]

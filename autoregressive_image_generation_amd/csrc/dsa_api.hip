@@ -1,0 +1,398 @@
+// C ABI of libdsa (declared in include/dsa.h): state sizing and validation,
+// the per-step resolution of Algorithm 1's phases (page 4, Section 4), and the
+// launches.  Every check runs on the host before anything is enqueued, so a
+// failing call has no side effects.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(DSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+enum Kind { KIND_SPARSE = 1, KIND_DENSE = 2 };
+
+}  // namespace
+
+struct dsa_state {
+    int kind;
+    int batch, heads, D, L_p, N_r, N_att, S, dtype, L_max;
+    int lanes, N_rw, N_attw;
+    long long lane_rows;
+    char* ws;
+    size_t ws_bytes;
+    size_t list_off;
+    hipStream_t stream;
+    int t;
+    int prompt_done;
+    const void* pend_k;
+    const void* pend_v;
+    int waves;
+};
+
+namespace {
+
+size_t elem_size(int dtype) { return dtype == DSA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Common shape checks; returns 0 or a status with the message set.
+int check_common(int batch, int L_p, int heads, int head_dim, int dtype) {
+    if (batch < 1) return fail(DSA_E_INVAL, "batch must be >= 1 (got %d)", batch);
+    if (heads < 1) return fail(DSA_E_INVAL, "heads must be >= 1 (got %d)", heads);
+    if (head_dim != 64 && head_dim != 128) return fail(DSA_E_INVAL, "head_dim must be 64 or 128 (got %d)", head_dim);
+    if (L_p < 0) return fail(DSA_E_INVAL, "L_p must be >= 0 (got %d)", L_p);
+    if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_E_INVAL, "dtype must be DSA_F32 or DSA_BF16");
+    if ((long long)batch * heads > (1ll << 30)) return fail(DSA_E_INVAL, "batch * heads too large");
+    return 0;
+}
+
+int check_sparse(int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink, int dtype) {
+    int rc = check_common(batch, L_p, heads, head_dim, dtype);
+    if (rc) return rc;
+    if (sink != 0 && sink != 4) return fail(DSA_E_INVAL, "sink must be 0 or 4 (got %d)", sink);
+    if (N_att < 1) return fail(DSA_E_INVAL, "N_att must be >= 1 (got %d)", N_att);
+    if (N_r < N_att) return fail(DSA_E_INVAL, "N_r (%d) must be >= N_att (%d)", N_r, N_att);
+    if (N_r > 32767) return fail(DSA_E_INVAL, "N_r must be <= 32767 (got %d)", N_r);
+    if (sink && N_att <= sink) return fail(DSA_E_INVAL, "sink = %d needs N_att > %d (got %d)", sink, sink, N_att);
+    if (N_att - sink > DSA_MAX_ATTEND)
+        return fail(DSA_E_INVAL, "N_att - sink must be <= %d (got %d)", DSA_MAX_ATTEND, N_att - sink);
+    return 0;
+}
+
+size_t kv_bytes(long long lanes, long long lane_rows, int D, int dtype) {
+    return align_up((size_t)lanes * (size_t)lane_rows * 2 * (size_t)D * elem_size(dtype));
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+    if (!ws) return fail(DSA_E_WORKSPACE, "workspace pointer is NULL");
+    if ((uintptr_t)ws % kAlign) return fail(DSA_E_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    if (have < need) return fail(DSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return 0;
+}
+
+int check_state(const dsa_state* st, int kind) {
+    if (!st) return fail(DSA_E_INVAL, "state is NULL");
+    if (kind && st->kind != kind)
+        return fail(DSA_E_INVAL, "state is a %s state", st->kind == KIND_SPARSE ? "sparse" : "dense");
+    return 0;
+}
+
+// Wavefronts per workgroup: enough waves in flight over the whole chip
+// (256 CUs) while keeping a few rows per thread group.
+int choose_waves(const dsa_state* st, long long rows) {
+    if (st->waves) return st->waves;
+    const int gpw = 64 / (st->D / (16 / (int)elem_size(st->dtype)));
+    int w = 1;
+    while (w < 16 && (long long)st->lanes * w < 8192 && rows >= 4ll * gpw * (2 * w)) w *= 2;
+    return w;
+}
+
+int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
+    if (st->prompt_done) return fail(DSA_E_ORDER, "prompt already appended");
+    if (st->L_p > 0) {
+        if (!k_p || !v_p) return fail(DSA_E_INVAL, "prompt pointers are NULL");
+        if (!aligned16(k_p) || !aligned16(v_p)) return fail(DSA_E_INVAL, "prompt pointers must be 16-byte aligned");
+    }
+    const bool init_list = st->kind == KIND_SPARSE && st->S == 0;
+    if (st->L_p > 0 || init_list) {
+        dsa::PromptArgs a;
+        a.k_p = k_p;
+        a.v_p = v_p;
+        a.kv = st->ws;
+        a.list = init_list ? reinterpret_cast<int16_t*>(st->ws + st->list_off) : nullptr;
+        a.lane_rows = st->lane_rows;
+        a.B = st->batch;
+        a.H = st->heads;
+        a.L_p = st->L_p;
+        a.N_attw = st->N_attw;
+        hipError_t e = dsa::launch_prompt(st->dtype, st->D, a, st->stream);
+        if (e != hipSuccess) return hip_fail(e, "prompt copy launch");
+    }
+    st->prompt_done = 1;
+    return DSA_OK;
+}
+
+int record_kv(dsa_state* st, const void* k_t, const void* v_t) {
+    if (!st->prompt_done) return fail(DSA_E_ORDER, "append the prompt first");
+    if (st->pend_k) return fail(DSA_E_ORDER, "a row is already appended for step %d", st->t);
+    if (st->kind == KIND_DENSE && st->t >= st->L_max)
+        return fail(DSA_E_INVAL, "dense cache full (L_max = %d)", st->L_max);
+    if (!k_t || !v_t) return fail(DSA_E_INVAL, "k_t / v_t is NULL");
+    if (!aligned16(k_t) || !aligned16(v_t)) return fail(DSA_E_INVAL, "k_t / v_t must be 16-byte aligned");
+    st->pend_k = k_t;
+    st->pend_v = v_t;
+    return DSA_OK;
+}
+
+int check_step(const dsa_state* st, const void* q_t, const float* out) {
+    if (!st->prompt_done) return fail(DSA_E_ORDER, "append the prompt first");
+    if (!st->pend_k) return fail(DSA_E_ORDER, "append the step's K/V before decoding step %d", st->t);
+    if (!q_t || !out) return fail(DSA_E_INVAL, "q_t / out is NULL");
+    if (!aligned16(q_t) || !aligned16(out)) return fail(DSA_E_INVAL, "q_t / out must be 16-byte aligned");
+    if (st->t == 0x7fffffff) return fail(DSA_E_INVAL, "step counter exhausted");
+    return 0;
+}
+
+void fill_common(const dsa_state* st, const void* q_t, float* out, dsa::DecodeArgs& a) {
+    memset(&a, 0, sizeof(a));
+    a.kv = st->ws;
+    a.q = q_t;
+    a.k_new = st->pend_k;
+    a.v_new = st->pend_v;
+    a.out = out;
+    a.lane_rows = st->lane_rows;
+    a.lanes = st->lanes;
+    a.L_p = st->L_p;
+    a.t = st->t;
+    a.scale_log2e = 1.4426950408889634 / sqrt((double)st->D);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
+                                 int dtype) {
+    if (check_sparse(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype)) return 0;
+    const long long lanes = (long long)batch * heads;
+    return kv_bytes(lanes, (long long)L_p + N_r, head_dim, dtype) +
+           align_up((size_t)lanes * (size_t)(N_att - sink) * sizeof(int16_t));
+}
+
+int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
+                   int dtype, void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!out) return fail(DSA_E_INVAL, "out handle pointer is NULL");
+    int rc = check_sparse(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype);
+    if (rc) return rc;
+    const size_t need = dsa_state_workspace_bytes(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype);
+    rc = check_workspace(d_workspace, workspace_bytes, need);
+    if (rc) return rc;
+    dsa_state* st = new (std::nothrow) dsa_state();
+    if (!st) return fail(DSA_E_NOMEM, "host allocation failed");
+    st->kind = KIND_SPARSE;
+    st->batch = batch;
+    st->heads = heads;
+    st->D = head_dim;
+    st->L_p = L_p;
+    st->N_r = N_r;
+    st->N_att = N_att;
+    st->S = sink;
+    st->dtype = dtype;
+    st->L_max = 0;
+    st->lanes = batch * heads;
+    st->N_rw = N_r - sink;
+    st->N_attw = N_att - sink;
+    st->lane_rows = (long long)L_p + N_r;
+    st->ws = static_cast<char*>(d_workspace);
+    st->ws_bytes = workspace_bytes;
+    st->list_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    st->stream = static_cast<hipStream_t>(hip_stream);
+    *out = st;
+    return DSA_OK;
+}
+
+int dsa_set_stream(dsa_state* st, void* hip_stream) {
+    int rc = check_state(st, 0);
+    if (rc) return rc;
+    st->stream = static_cast<hipStream_t>(hip_stream);
+    return DSA_OK;
+}
+
+int dsa_append_prompt(dsa_state* st, const void* k_p, const void* v_p) {
+    int rc = check_state(st, KIND_SPARSE);
+    return rc ? rc : launch_prompt(st, k_p, v_p);
+}
+
+int dsa_append_kv(dsa_state* st, const void* k_t, const void* v_t) {
+    int rc = check_state(st, KIND_SPARSE);
+    return rc ? rc : record_kv(st, k_t, v_t);
+}
+
+int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) {
+    int rc = check_state(st, KIND_SPARSE);
+    if (rc) return rc;
+    rc = check_step(st, q_t, out);
+    if (rc) return rc;
+    if (trace && ((uintptr_t)trace & 7u)) return fail(DSA_E_INVAL, "trace must be 8-byte aligned");
+
+    dsa::DecodeArgs a;
+    fill_common(st, q_t, out, a);
+    const int t = st->t, S = st->S, N_rw = st->N_rw, N_attw = st->N_attw;
+    const int tw = t - S;  // step inside the non-sink sequence
+    a.list = reinterpret_cast<int16_t*>(st->ws + st->list_off);
+    a.trace = trace;
+    a.S = S;
+    a.N_rw = N_rw;
+    a.N_attw = N_attw;
+    // Window entries attended at t: min(t' + 1, N_att') (phase 1 grows, then fixed).
+    a.n_list = tw < 0 ? 0 : std::min(tw + 1, N_attw);
+    a.n_sink = std::min(t + 1, S);
+    // Phase 2 selects while |skip_idx| < N_r - N_att: steps N_att-1 .. N_r-2.
+    a.select = (t >= st->N_att - 1 && t <= st->N_r - 2) ? 1 : 0;
+    // Offset t'+1 enters the window at step t+1 while the window still grows.
+    a.add_off = (tw + 1 >= 0 && tw + 1 <= N_rw - 1) ? tw + 1 : -1;
+    a.base = tw >= 0 ? tw % N_rw : 0;
+    a.self_row = t < S ? t : S + a.base;
+    // Phase 3 (t >= N_r): the oldest non-sink entry t - (N_r - S) leaves.
+    a.evicted = t >= st->N_r ? t - N_rw : -1;
+
+    const int waves = choose_waves(st, (long long)st->L_p + S + N_attw);
+    hipError_t e = dsa::launch_decode(dsa::MODE_SPARSE, st->dtype, st->D, waves, a, st->stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse decode launch");
+    st->pend_k = st->pend_v = nullptr;
+    st->t += 1;
+    return DSA_OK;
+}
+
+int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_t* h_count) {
+    int rc = check_state(st, KIND_SPARSE);
+    if (rc) return rc;
+    const int tw = st->t - st->S;
+    const int n = tw < 0 ? 0 : std::min(tw + 1, st->N_attw);
+    if (h_offsets || h_count) {
+        std::vector<int16_t> buf;
+        try {
+            buf.resize((size_t)st->lanes * st->N_attw);
+        } catch (...) {
+            return fail(DSA_E_NOMEM, "host allocation failed");
+        }
+        hipError_t e = hipStreamSynchronize(st->stream);
+        if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+        e = hipMemcpy(buf.data(), st->ws + st->list_off, buf.size() * sizeof(int16_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "list copy");
+        for (int l = 0; l < st->lanes; ++l) {
+            int16_t* src = buf.data() + (size_t)l * st->N_attw;
+            std::sort(src, src + n);
+            if (h_offsets) {
+                int16_t* dst = h_offsets + (size_t)l * st->N_attw;
+                for (int j = 0; j < st->N_attw; ++j) dst[j] = j < n ? src[j] : (int16_t)-1;
+            }
+            if (h_count) h_count[l] = n;
+        }
+    } else {
+        hipError_t e = hipStreamSynchronize(st->stream);
+        if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    }
+    if (h_t) *h_t = st->t;
+    return DSA_OK;
+}
+
+size_t dense_state_workspace_bytes(int batch, int L_p, int L_max, int heads, int head_dim, int dtype) {
+    if (check_common(batch, L_p, heads, head_dim, dtype) || L_max < 1) return 0;
+    return kv_bytes((long long)batch * heads, (long long)L_p + L_max, head_dim, dtype);
+}
+
+int dense_state_init(dsa_state** out, int batch, int L_p, int L_max, int heads, int head_dim, int dtype,
+                     void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!out) return fail(DSA_E_INVAL, "out handle pointer is NULL");
+    int rc = check_common(batch, L_p, heads, head_dim, dtype);
+    if (rc) return rc;
+    if (L_max < 1) return fail(DSA_E_INVAL, "L_max must be >= 1 (got %d)", L_max);
+    if ((long long)L_p + L_max > 0x7fffffffll) return fail(DSA_E_INVAL, "L_p + L_max too large");
+    rc = check_workspace(d_workspace, workspace_bytes,
+                         dense_state_workspace_bytes(batch, L_p, L_max, heads, head_dim, dtype));
+    if (rc) return rc;
+    dsa_state* st = new (std::nothrow) dsa_state();
+    if (!st) return fail(DSA_E_NOMEM, "host allocation failed");
+    st->kind = KIND_DENSE;
+    st->batch = batch;
+    st->heads = heads;
+    st->D = head_dim;
+    st->L_p = L_p;
+    st->dtype = dtype;
+    st->L_max = L_max;
+    st->lanes = batch * heads;
+    st->lane_rows = (long long)L_p + L_max;
+    st->ws = static_cast<char*>(d_workspace);
+    st->ws_bytes = workspace_bytes;
+    st->stream = static_cast<hipStream_t>(hip_stream);
+    *out = st;
+    return DSA_OK;
+}
+
+int dense_append_prompt(dsa_state* st, const void* k_p, const void* v_p) {
+    int rc = check_state(st, KIND_DENSE);
+    return rc ? rc : launch_prompt(st, k_p, v_p);
+}
+
+int dense_append_kv(dsa_state* st, const void* k_t, const void* v_t) {
+    int rc = check_state(st, KIND_DENSE);
+    return rc ? rc : record_kv(st, k_t, v_t);
+}
+
+int dense_decode_step(dsa_state* st, const void* q_t, float* out) {
+    int rc = check_state(st, KIND_DENSE);
+    if (rc) return rc;
+    rc = check_step(st, q_t, out);
+    if (rc) return rc;
+    dsa::DecodeArgs a;
+    fill_common(st, q_t, out, a);
+    a.self_row = st->t;
+    const int waves = choose_waves(st, (long long)st->L_p + st->t + 1);
+    hipError_t e = dsa::launch_decode(dsa::MODE_DENSE, st->dtype, st->D, waves, a, st->stream);
+    if (e != hipSuccess) return hip_fail(e, "dense decode launch");
+    st->pend_k = st->pend_v = nullptr;
+    st->t += 1;
+    return DSA_OK;
+}
+
+int dsa_set_waves(dsa_state* st, int waves_per_lane) {
+    int rc = check_state(st, 0);
+    if (rc) return rc;
+    if (waves_per_lane != 0 && waves_per_lane != 1 && waves_per_lane != 2 && waves_per_lane != 4 &&
+        waves_per_lane != 8 && waves_per_lane != 16)
+        return fail(DSA_E_INVAL, "waves_per_lane must be 0, 1, 2, 4, 8 or 16 (got %d)", waves_per_lane);
+    st->waves = waves_per_lane;
+    return DSA_OK;
+}
+
+int dsa_state_step(const dsa_state* st) {
+    int rc = check_state(st, 0);
+    return rc ? rc : st->t;
+}
+
+int dsa_state_destroy(dsa_state* st) {
+    delete st;
+    return DSA_OK;
+}
+
+const char* dsa_strerror(int code) {
+    switch (code) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_E_INVAL: return "DSA_E_INVAL: invalid argument";
+        case DSA_E_ORDER: return "DSA_E_ORDER: call out of order";
+        case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing, misaligned or too small";
+        case DSA_E_HIP: return "DSA_E_HIP: HIP runtime error";
+        case DSA_E_NOMEM: return "DSA_E_NOMEM: host allocation failed";
+        default: return "unknown dsa_status";
+    }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI layer (dsa_api.hip) and the kernels
+// (dsa_kernels.hip).  Not installed; the public contract is include/dsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1 };
+
+// Everything one decode launch needs.  Host-computed per step: all lanes of a
+// state share t, so the phase logic of Algorithm 1 (page 4, Section 4) is
+// resolved here once and the kernel only sees its consequences.
+struct DecodeArgs {
+    const void* kv;        // cache base: [lanes][lane_rows][2][D] (K row then V row)
+    int16_t* list;         // sparse: [lanes][N_attw] attended window offsets (t - position)
+    const void* q;         // [lanes][D]
+    const void* k_new;     // [lanes][D], the step's appended key
+    const void* v_new;     // [lanes][D]
+    float* out;            // [lanes][D]
+    int32_t* trace;        // sparse, nullable: [lanes][2]
+    long long lane_rows;   // rows per lane in the cache
+    int lanes;
+    int L_p;
+    int S;                 // sink count (0 or 4)
+    int N_rw;              // ring length for non-sink entries: N_r - S
+    int N_attw;            // attended non-sink budget: N_att - S
+    int t;                 // decode step
+    int n_list;            // sparse: entries of the list valid at this step
+    int n_sink;            // sparse: sink positions attended at this step (min(t+1, S))
+    int select;            // sparse: 1 if this step picks a new skip entry
+    int add_off;           // sparse: offset entering the list for step t+1, or -1
+    int base;              // sparse: (t - S) mod N_rw, ring index of the current token
+    int self_row;          // cache row (after the prompt rows) the appended K/V goes to
+    int evicted;           // sparse: position evicted at this step, or -1
+    double scale_log2e;    // log2(e) / sqrt(D)
+};
+
+struct PromptArgs {
+    const void* k_p;       // [B][L_p][H][D]
+    const void* v_p;
+    void* kv;
+    int16_t* list;         // nullable: when set, list[lane * N_attw] = 0 for every lane
+    long long lane_rows;
+    int B, H, L_p, N_attw;
+};
+
+hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prompt(int dtype, int D, const PromptArgs& a, hipStream_t s);
+
+}  // namespace dsa

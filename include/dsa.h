@@ -1,0 +1,167 @@
+/*
+ * dsa.h - C ABI of libdsa: decode-step diagonal-aware sparse attention and its
+ * dense comparison point, on AMD MI355X (gfx950).
+ *
+ * The operation is Algorithm 1 ("Diagonal-Aware Sparse Attention") of
+ * "Understanding and Exploiting Diagonal Attention Sparsity in Autoregressive
+ * Image Generation" (arxiv 2609.19702, Section 4), for every (sequence, head)
+ * lane of one transformer layer; one state per layer.  Per decode step t every
+ * lane attends its whole prompt KV (L_p rows) plus N_att of the last N_r
+ * decode entries; the skipped set grows by one lowest-score entry per step
+ * during phase 2 and moves +1 along the attention diagonal every step; once
+ * t >= N_r the oldest decode entry is evicted (Section 4, "Detailed
+ * explanation").  sink = 4 selects the Diagonal+Sink4 variant (Section 5.1,
+ * "Our methods"): decode positions 0..3 stay attended for good and the
+ * algorithm runs on the rest with budgets N_r - 4 and N_att - 4.
+ *
+ * Conventions
+ *   - Lanes: lane = b * heads + h.  All lanes of a state share the step t.
+ *   - Tensors passed per step are device pointers, row-major [batch][heads][head_dim]
+ *     in the state's KV dtype (q, k, v) or fp32 (out).  The prompt is
+ *     [batch][L_p][heads][head_dim].  Pointers must be 16-byte aligned.
+ *   - Softmax scale is 1 / sqrt(head_dim); one softmax over prompt + selected
+ *     decode rows; accumulation in fp32, the raw q.k logits in fp64.
+ *   - Argmin: the lowest raw logit q.k among the attended non-sink window
+ *     entries of the step (the current token included); ties go to the lowest
+ *     decode position.  Selections happen at t = N_att-1 .. N_r-2.
+ *   - Memory: the caller owns the device workspace (size from the
+ *     *_workspace_bytes call, 256-byte aligned) and every tensor.  The library
+ *     owns only the small host handle, freed by dsa_state_destroy.
+ *   - Execution: every call is asynchronous on the state's HIP stream, except
+ *     dsa_read_state, which synchronises it.  Arguments are checked on the host
+ *     before anything is enqueued; a failing call returns a negative dsa_status,
+ *     leaves the state unchanged and enqueues nothing.  dsa_last_error() gives
+ *     a message for the calling thread's last failure.
+ *   - Order: *_append_prompt once; then for each step one *_append_kv followed
+ *     by one *_decode_step.  Anything else returns DSA_E_ORDER.
+ *   - dsa_append_kv / dense_append_kv record the pointers only; the following
+ *     decode step writes the new row into the cache (overwriting the evicted
+ *     entry in phase 3) in the same launch.  k_t and v_t must stay valid until
+ *     that step has run on the stream.
+ *   - Calls on one state must not run concurrently from several host threads.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dsa_state dsa_state;
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_E_INVAL = -1,     /* bad argument: sizes, dtype, null or misaligned pointer, capacity */
+    DSA_E_ORDER = -2,     /* call out of order (see Order above) */
+    DSA_E_WORKSPACE = -3, /* workspace missing, too small or misaligned */
+    DSA_E_HIP = -4,       /* the HIP runtime reported an error (detail in dsa_last_error) */
+    DSA_E_NOMEM = -5      /* host allocation failed */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+/* Largest N_att - sink the sparse kernel supports (its index list lives in LDS). */
+#define DSA_MAX_ATTEND 8192
+
+/*
+ * Device workspace bytes of a sparse state: per lane a cache of L_p prompt
+ * rows plus an N_r-entry ring of decode rows (each row K then V, head_dim
+ * elements each), which is the footprint bound N_r + L_p of Section 4 "Cost
+ * analysis", plus the per-lane list of attended window offsets.  Returns 0
+ * when the parameters are invalid (same rules as dsa_state_init).
+ */
+size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
+                                 int dtype);
+
+/*
+ * Create a sparse state.  Parameters: batch >= 1, heads >= 1, head_dim in
+ * {64, 128}, L_p >= 0, 1 <= N_att <= N_r <= 32767, sink in {0, 4} (sink = 4
+ * needs N_att >= 5), N_att - sink <= DSA_MAX_ATTEND, dtype a dsa_dtype.
+ * d_workspace: device memory of at least dsa_state_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller and used by this state alone until
+ * destroy.  hip_stream: the hipStream_t every call of this state enqueues on
+ * (NULL = the null stream).  On success *out receives the handle.
+ */
+int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
+                   int dtype, void* d_workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Change the stream later calls enqueue on. */
+int dsa_set_stream(dsa_state* st, void* hip_stream);
+
+/*
+ * Copy the prompt KV (Algorithm 1 input K_p, V_p), [batch][L_p][heads][head_dim]
+ * each, into the state's cache.  Must be the first call after init; with
+ * L_p = 0 the pointers may be NULL.
+ */
+int dsa_append_prompt(dsa_state* st, const void* k_p, const void* v_p);
+
+/* Record the step's new key and value rows, [batch][heads][head_dim] each. */
+int dsa_append_kv(dsa_state* st, const void* k_t, const void* v_t);
+
+/*
+ * One decode step t of Algorithm 1 for all lanes, in one kernel launch: write
+ * the appended row into the ring (evicting t - N_r in phase 3), gather the
+ * prompt rows and the attended window rows, softmax attention into
+ * out [batch][heads][head_dim] (fp32), and during t in [N_att-1, N_r-2] pick
+ * the window entry with the lowest logit and add it to the skip set (it is
+ * skipped from step t+1 on).  q_t: [batch][heads][head_dim] in the KV dtype.
+ * trace (nullable, device): [batch][heads][2] int32 = (position selected at
+ * this step or -1, position evicted at this step or -1).  Advances t by one.
+ */
+int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace);
+
+/*
+ * Copy the lane state to the host; synchronises the stream.  h_t receives the
+ * index of the next step.  h_offsets ([batch*heads][N_att - sink], nullable)
+ * receives, per lane, the window entries the next step will attend, as
+ * offsets t - position in ascending order, padded with -1; h_count
+ * ([batch*heads], nullable) their number.  Sinks are not listed.
+ */
+int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_t* h_count);
+
+/* Device workspace bytes of a dense state holding L_p + L_max rows per lane; 0 if invalid. */
+size_t dense_state_workspace_bytes(int batch, int L_p, int L_max, int heads, int head_dim, int dtype);
+
+/*
+ * Create a dense state ("No sparsity", Section 2.3 (1)): step t attends every
+ * prompt row and decode positions 0..t.  L_max >= 1 is the number of decode
+ * steps the cache holds.  Other parameters as dsa_state_init.
+ */
+int dense_state_init(dsa_state** out, int batch, int L_p, int L_max, int heads, int head_dim, int dtype,
+                     void* d_workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Prompt and per-step rows of a dense state: same contracts as the dsa_ calls. */
+int dense_append_prompt(dsa_state* st, const void* k_p, const void* v_p);
+int dense_append_kv(dsa_state* st, const void* k_t, const void* v_t);
+
+/* One dense decode step: out [batch][heads][head_dim] fp32.  Fails with
+ * DSA_E_INVAL once L_max steps have run. */
+int dense_decode_step(dsa_state* st, const void* q_t, float* out);
+
+/*
+ * Workgroup size of the decode kernels, in 64-wide wavefronts per lane:
+ * 1, 2, 4, 8 or 16, or 0 for the library's choice.  Results do not depend on
+ * it except for fp32 rounding order in the softmax sums.
+ */
+int dsa_set_waves(dsa_state* st, int waves_per_lane);
+
+/* Next step index of a sparse or dense state (or a negative dsa_status). */
+int dsa_state_step(const dsa_state* st);
+
+/* Free the host handle (the workspace stays the caller's).  NULL is a no-op. */
+int dsa_state_destroy(dsa_state* st);
+
+/* Static name of a dsa_status code. */
+const char* dsa_strerror(int code);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

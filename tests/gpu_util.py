@@ -1,0 +1,118 @@
+"""Drive the GPU library through its C ABI for parity tests, and compare one
+lane against the oracle in lockstep."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import autoregressive_image_generation_amd as dsa
+import oracle
+import synth
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+NEAR_TIE = 1e-6
+
+
+def tol(w):
+    return F32_TOL if w.dtype == synth.F32 else BF16_TOL
+
+
+def to_dev(arr, dev):
+    if arr.dtype == np.uint16:
+        arr = arr.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+
+def device_inputs(w, layer, T, dev):
+    q = to_dev(w.decode(layer, synth.Q, 0, T), dev)
+    k = to_dev(w.decode(layer, synth.K, 0, T), dev)
+    v = to_dev(w.decode(layer, synth.V, 0, T), dev)
+    kp = to_dev(w.prompt(layer, synth.KP), dev)
+    vp = to_dev(w.prompt(layer, synth.VP), dev)
+    return q, k, v, kp, vp
+
+
+def run_sparse(w, inputs, T, dev, waves=0, read_every=0):
+    """T steps of one layer.  Returns out [T][B][H][D] (device), trace [T][B][H][2]
+    (host) and, with read_every > 0, {t: (offsets, counts)} read after step t."""
+    q, k, v, kp, vp = inputs
+    B, H, D = w.batch, w.heads, w.head_dim
+    nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes, stream)
+    dsa.dsa_set_waves(st, waves)
+    out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
+    trace = torch.empty((T, B, H, 2), dtype=torch.int32, device=dev)
+    dsa.dsa_append_prompt(st, kp if w.L_p else None, vp if w.L_p else None)
+    step_in = q[0].numel() * q.element_size()
+    step_out = out[0].numel() * 4
+    step_tr = trace[0].numel() * 4
+    qb, kb, vb, ob, tb = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), trace.data_ptr()
+    reads = {}
+    for t in range(T):
+        dsa.dsa_append_kv(st, kb + t * step_in, vb + t * step_in)
+        dsa.dsa_decode_step(st, qb + t * step_in, ob + t * step_out, tb + t * step_tr)
+        if read_every and (t % read_every == 0 or t == T - 1):
+            t_next, offs, cnt = dsa.dsa_read_state(st)
+            assert t_next == t + 1
+            reads[t] = (offs.copy(), cnt.copy())
+    torch.cuda.synchronize(dev)
+    dsa.dsa_state_destroy(st)
+    return out, trace.cpu().numpy(), reads
+
+
+def run_dense(w, inputs, T, dev, waves=0):
+    q, k, v, kp, vp = inputs
+    B, H, D = w.batch, w.heads, w.head_dim
+    nbytes = dsa.dense_state_workspace_bytes(B, w.L_p, T, H, D, w.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    st = dsa.dense_state_init(B, w.L_p, T, H, D, w.dtype, ws, nbytes, torch.cuda.current_stream(dev))
+    dsa.dsa_set_waves(st, waves)
+    out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
+    dsa.dense_append_prompt(st, kp if w.L_p else None, vp if w.L_p else None)
+    for t in range(T):
+        dsa.dense_append_kv(st, k[t], v[t])
+        dsa.dense_decode_step(st, q[t], out[t])
+    torch.cuda.synchronize(dev)
+    dsa.dsa_state_destroy(st)
+    return out
+
+
+def lane_inputs_from(w, layer, b, h, T):
+    return oracle.lane_inputs(w, layer, b, h, T)
+
+
+def check_lane(w, ins, out_lane, trace_lane, stats):
+    """Lockstep parity of one lane: the oracle follows the GPU's choices and
+    reports its own; indices must agree except near-ties (relative logit gap
+    below 1e-6), which are counted; outputs within the dtype's tolerance."""
+    T = out_lane.shape[0]
+    gpu_choice = trace_lane[:, 0].astype(np.int32)
+    sel = gpu_choice >= 0
+    follow = np.where(sel, gpu_choice, 0).astype(np.int32)
+    ref = oracle.run_lane(w.L_p, w.N_r, w.N_att, w.sink, *ins, follow=follow)
+    # selection happens at exactly the oracle's steps
+    np.testing.assert_array_equal(sel, ref["choice"] >= 0)
+    np.testing.assert_array_equal(trace_lane[:, 1], ref["evicted"])
+    diff = np.nonzero(gpu_choice != ref["choice"])[0]
+    for t in diff:
+        g = abs(float(ref["gap"][t]))
+        assert g < NEAR_TIE, "step %d: GPU chose %d, oracle %d, relative gap %.3g" % (
+            t, gpu_choice[t], ref["choice"][t], g)
+    stats["near_ties"] = stats.get("near_ties", 0) + len(diff)
+    stats["selections"] = stats.get("selections", 0) + int(sel.sum())
+    err = float(np.abs(out_lane.astype(np.float64) - ref["out"]).max()) if T else 0.0
+    stats["max_err"] = max(stats.get("max_err", 0.0), err)
+    assert err <= tol(w), "max |out - oracle| = %.3g > %.3g" % (err, tol(w))
+    return ref
+
+
+def final_offsets(w, T, choices):
+    """Attended window offsets after T steps, from the offset closed form."""
+    S = w.sink
+    tw = T - S
+    D = {t - p for t, p in enumerate(choices) if p >= 0}
+    hi = min(tw, w.N_r - S - 1)
+    return sorted(d for d in range(0, hi + 1) if d not in D) if tw >= 0 else []

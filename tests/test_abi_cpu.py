@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dsa.h declares, sizes workspaces as documented, and rejects bad
+arguments and bad call orders on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import autoregressive_image_generation_amd as dsa
+from autoregressive_image_generation_amd import DsaError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, E_INVAL, E_ORDER, E_WORKSPACE, E_HIP, E_NOMEM = 0, -1, -2, -3, -4, -5
+FAKE_WS = 1 << 40  # an aligned address that is never dereferenced by these tests
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"})
+
+
+def test_library_exports_every_declared_function():
+    lib = dsa.library()
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(dsa.exported_symbols()) == names
+
+
+def test_strerror_names_every_status():
+    for code, key in [(OK, "DSA_OK"), (E_INVAL, "INVAL"), (E_ORDER, "ORDER"), (E_WORKSPACE, "WORKSPACE"),
+                      (E_HIP, "HIP"), (E_NOMEM, "NOMEM")]:
+        assert key in dsa.dsa_strerror(code)
+    assert "unknown" in dsa.dsa_strerror(-99)
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,L_p,N_r,N_att,H,D,S,dt", [
+    (96, 64, 288, 29, 32, 128, 0, 1),
+    (8, 96, 4050, 810, 32, 128, 4, 1),
+    (1, 16, 32, 8, 4, 64, 0, 0),
+    (3, 0, 5, 5, 1, 64, 0, 1),
+])
+def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
+    es = 2 if dt == 1 else 4
+    lanes = B * H
+    want = _align(lanes * (L_p + N_r) * 2 * D * es) + _align(lanes * (N_att - S) * 2)
+    assert dsa.dsa_state_workspace_bytes(B, L_p, N_r, N_att, H, D, S, dt) == want
+    assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * 2 * D * es)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 16, 32, 8, 4, 64, 0, 0),      # batch 0
+    (1, 16, 32, 8, 0, 64, 0, 0),      # heads 0
+    (1, 16, 32, 8, 4, 96, 0, 0),      # head_dim 96
+    (1, -1, 32, 8, 4, 64, 0, 0),      # negative prompt
+    (1, 16, 32, 0, 4, 64, 0, 0),      # N_att 0
+    (1, 16, 8, 9, 4, 64, 0, 0),       # N_att > N_r
+    (1, 16, 40000, 8, 4, 64, 0, 0),   # N_r beyond int16 offsets
+    (1, 16, 32, 4, 4, 64, 4, 0),      # sink 4 needs N_att > 4
+    (1, 16, 32, 8, 4, 64, 2, 0),      # sink must be 0 or 4
+    (1, 16, 32, 8, 4, 64, 0, 7),      # dtype
+    (1, 16, 20000, 9000, 4, 64, 0, 1),  # list beyond LDS capacity
+])
+def test_invalid_parameters_rejected(args):
+    assert dsa.dsa_state_workspace_bytes(*args) == 0
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_state_init(*args, FAKE_WS, 1 << 40)
+    assert e.value.code == E_INVAL
+
+
+def test_workspace_errors():
+    args = (2, 16, 32, 8, 4, 64, 0, 1)
+    need = dsa.dsa_state_workspace_bytes(*args)
+    for ws, nbytes in [(0, need), (FAKE_WS + 16, need), (FAKE_WS, need - 1)]:
+        with pytest.raises(DsaError) as e:
+            dsa.dsa_state_init(*args, ws, nbytes)
+        assert e.value.code == E_WORKSPACE
+    st = dsa.dsa_state_init(*args, FAKE_WS, need)
+    dsa.dsa_state_destroy(st)
+    with pytest.raises(DsaError) as e:
+        dsa.dense_state_init(2, 16, 64, 4, 64, 1, FAKE_WS, 10)
+    assert e.value.code == E_WORKSPACE
+    with pytest.raises(DsaError) as e:
+        dsa.dense_state_init(2, 16, 0, 4, 64, 1, FAKE_WS, 1 << 30)
+    assert e.value.code == E_INVAL
+
+
+def test_call_order_is_enforced_without_touching_the_device():
+    # L_p = 0 and sink = 4: the prompt call enqueues nothing, so the whole
+    # order machinery can run on a host without a GPU.
+    args = (1, 0, 16, 8, 2, 128, 4, 1)
+    need = dsa.dsa_state_workspace_bytes(*args)
+    st = dsa.dsa_state_init(*args, FAKE_WS, need)
+    buf = FAKE_WS + (1 << 20)
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_kv(st, buf, buf)
+    assert e.value.code == E_ORDER
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_decode_step(st, buf, buf)
+    assert e.value.code == E_ORDER
+    dsa.dsa_append_prompt(st, None, None)
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_prompt(st, None, None)
+    assert e.value.code == E_ORDER
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_decode_step(st, buf, buf)          # no K/V appended for this step
+    assert e.value.code == E_ORDER
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_kv(st, buf + 8, buf)        # misaligned
+    assert e.value.code == E_INVAL
+    dsa.dsa_append_kv(st, buf, buf)
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_kv(st, buf, buf)            # second append for the same step
+    assert e.value.code == E_ORDER
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_decode_step(st, buf, buf, buf + 4)  # misaligned trace
+    assert e.value.code == E_INVAL
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_decode_step(st, None, buf)
+    assert e.value.code == E_INVAL
+    assert dsa.dsa_state_step(st) == 0              # failed calls left the state alone
+    with pytest.raises(DsaError) as e:
+        dsa.dense_decode_step(st, buf, buf)         # wrong state kind
+    assert e.value.code == E_INVAL
+    for w in (3, 32, -1):
+        with pytest.raises(DsaError):
+            dsa.dsa_set_waves(st, w)
+    for w in (0, 1, 2, 4, 8, 16):
+        dsa.dsa_set_waves(st, w)
+    assert "aligned" in dsa.dsa_last_error() or dsa.dsa_last_error() != ""
+    dsa.dsa_state_destroy(st)
+
+
+def test_null_state_and_handle():
+    lib = dsa.library()
+    assert lib.dsa_append_kv(None, None, None) == E_INVAL
+    assert lib.dsa_decode_step(None, None, None, None) == E_INVAL
+    assert lib.dsa_state_step(None) == E_INVAL
+    assert lib.dsa_state_destroy(None) == OK
+    assert lib.dsa_state_init(None, 1, 1, 4, 2, 1, 64, 0, 0, ctypes.c_void_p(FAKE_WS), 1 << 30, None) == E_INVAL

@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Indices (argmin choices, evictions, attended lists) must match exactly;
+choices may differ only at near-ties (relative logit gap < 1e-6), which are
+counted and printed.  Outputs: |gpu - oracle| <= 1e-4 (fp32 KV) or 2e-2 (bf16 KV).
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from closed_form import attended_sets, falling_expected, rising_expected
+from gpu_util import (check_lane, device_inputs, final_offsets, lane_inputs_from, run_dense, run_sparse, tol,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tiny(**kw):
+    return synth.WORKLOADS["tiny_fp32"].with_(**kw)
+
+
+def _parity(w, T=None, lanes=None, waves=0, read_every=0, layer=0):
+    T = w.L_dec if T is None else T
+    say("parity %s T=%d N_r=%d N_att=%d sink=%d waves=%d" % (w.name, T, w.N_r, w.N_att, w.sink, waves))
+    ins = device_inputs(w, layer, T, DEV)
+    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every)
+    lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    stats = {}
+    for (b, h) in lanes:
+        li = lane_inputs_from(w, layer, b, h, T)
+        ref = check_lane(w, li, out[:, b, h, :].cpu().numpy(), trace[:, b, h, :], stats)
+        if read_every:
+            choices = [int(c) for c in trace[:, b, h, 0]]
+            lane = b * w.heads + h
+            for t, (offs, cnt) in reads.items():
+                want = final_offsets(w, t + 1, choices[: t + 1])
+                got = [int(x) for x in offs[lane][: cnt[lane]]]
+                assert got == want, (t, got, want)
+    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g" % (
+        len(lanes), stats["selections"], stats["near_ties"], stats["max_err"]))
+    return out, trace, stats
+
+
+# ------------------------------------------------------------ tiny fp32, every lane and step
+def test_tiny_fp32_full_decode_all_phases():
+    _parity(tiny(), read_every=1)
+
+
+@pytest.mark.parametrize("S", [0, 4])
+def test_tiny_fp32_equal_budgets(S):
+    # N_r = N_att = L_dec: dense; N_r = N_att = 32: sliding window / StreamingLLM
+    _parity(tiny(N_r=64, N_att=64, sink=S), read_every=7)
+    _parity(tiny(N_r=32, N_att=32, sink=S), read_every=7)
+
+
+def test_tiny_fp32_sink4():
+    _parity(tiny(sink=4), read_every=1)
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
+def test_tiny_every_workgroup_size(waves):
+    _parity(tiny(), waves=waves)
+
+
+@pytest.mark.parametrize("dt,D", [(synth.BF16, 64), (synth.BF16, 128), (synth.F32, 128)])
+def test_other_dtypes_and_head_dims(dt, D):
+    _parity(tiny(dtype=dt, head_dim=D, batch=3, heads=5), read_every=5)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(L_p=0),                         # no prompt
+    dict(N_att=1),                       # one attended window entry
+    dict(N_att=2, N_r=3),                # tiny ring
+    dict(N_att=5, N_r=6, sink=4),        # one non-sink slot attended
+    dict(N_att=31),                      # one selection only
+    dict(batch=7, heads=3, L_p=5),       # ragged lane count and prompt
+])
+def test_edge_cases(kw):
+    _parity(tiny(**kw), read_every=3)
+
+
+def test_deterministic_across_runs():
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=2)
+    ins = device_inputs(w, 0, w.L_dec, DEV)
+    o1, t1, _ = run_sparse(w, ins, w.L_dec, DEV)
+    o2, t2, _ = run_sparse(w, ins, w.L_dec, DEV)
+    assert torch.equal(o1, o2)
+    np.testing.assert_array_equal(t1, t2)
+
+
+# ------------------------------------------------------------ engineered closed forms on the GPU
+def _engineered_run(w, q, kp, vp, k, v):
+    T, d = q.shape
+    D = w.head_dim
+
+    def pad(x):
+        y = np.zeros((x.shape[0], D), np.float32)
+        y[:, :d] = x
+        return y
+
+    qq, kk, vv = pad(q), pad(k), pad(v)
+    ins = (to_dev(qq[:, None, None, :], DEV), to_dev(kk[:, None, None, :], DEV), to_dev(vv[:, None, None, :], DEV),
+           to_dev(pad(kp)[None, :, None, :], DEV), to_dev(pad(vp)[None, :, None, :], DEV))
+    out, trace, reads = run_sparse(w, ins, T, DEV, read_every=1)
+    return out.cpu().numpy()[:, 0, 0, :d], trace[:, 0, 0, :], reads
+
+
+def test_worked_example_on_gpu():
+    with open(os.path.join(GOLDEN, "worked_example_nr7_natt4.json")) as f:
+        g = json.load(f)
+    e = g["engineered_inputs"]
+    T, d, L_p = e["T"], e["d"], e["L_p"]
+    q = np.zeros((T, d))
+    for t in range(T):
+        q[t, {3: 0, 4: 1}.get(t, 2)] = 1.0
+    k = np.zeros((T, d))
+    k[:, 0], k[:, 1], k[:, 2] = e["a"], e["b"], e["c"]
+    rng = np.random.default_rng(1)
+    v, kp, vp = rng.normal(size=(T, d)), rng.normal(size=(L_p, d)), rng.normal(size=(L_p, d))
+    w = tiny(batch=1, heads=1, L_p=L_p, L_dec=T, N_r=7, N_att=4)
+    out, trace, reads = _engineered_run(w, q, kp, vp, k, v)
+    for step in g["expected"]["steps"]:
+        t = step["t"]
+        assert trace[t, 0] == step["selected"], t
+        assert trace[t, 1] == step["evicted"], t
+    exp = {s["t"]: s["attended"] for s in g["expected"]["steps"]}
+    for t in range(T - 1):
+        offs, cnt = reads[t]
+        got = sorted(t + 1 - int(x) for x in offs[0][: cnt[0]])
+        assert got == exp[t + 1], (t + 1, got)
+
+
+@pytest.mark.parametrize("S", [0, 4])
+@pytest.mark.parametrize("direction", [+1, -1])
+def test_monotone_scores_on_gpu(direction, S):
+    from closed_form import monotone_inputs
+
+    N_r, N_att, T = 20, 9, 47
+    q, kp, vp, k, v = monotone_inputs(T, 8, 3, direction)
+    w = tiny(batch=1, heads=1, L_p=3, L_dec=T, N_r=N_r, N_att=N_att, sink=S)
+    out, trace, reads = _engineered_run(w, q, kp, vp, k, v)
+    expect = rising_expected if direction > 0 else falling_expected
+    for t in range(T - 1):
+        offs, cnt = reads[t]
+        window = sorted(t + 1 - int(x) for x in offs[0][: cnt[0]])
+        sinks = list(range(min(t + 2, S)))
+        assert sinks + window == expect(t + 1, N_r, N_att, S), t + 1
+
+
+# ------------------------------------------------------------ dense kernel
+@pytest.mark.parametrize("dt,D", [(synth.F32, 64), (synth.BF16, 128)])
+def test_dense_matches_oracle(dt, D):
+    w = tiny(dtype=dt, head_dim=D, batch=2)
+    T = w.L_dec
+    ins = device_inputs(w, 0, T, DEV)
+    out = run_dense(w, ins, T, DEV).cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.heads):
+            li = lane_inputs_from(w, 0, b, h, T)
+            ref = oracle.run_dense_lane(w.L_p, *li)
+            err = np.abs(out[:, b, h, :] - ref).max()
+            assert err <= tol(w), err
+
+
+# ------------------------------------------------------------ the full-size workloads (one layer)
+FULL = ["janus_pro_1b", "janus_pro_7b", "lumina_mgpt_7b_1024", "hires_8100_sink4"]
+
+
+def _sample_lanes(w, n, seed):
+    rng = np.random.default_rng(seed)
+    lanes = {(0, 0), (w.batch - 1, w.heads - 1)}
+    while len(lanes) < n:
+        lanes.add((int(rng.integers(w.batch)), int(rng.integers(w.heads))))
+    return sorted(lanes)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload_sampled_lanes(name):
+    """Full batch x heads x L_dec of one layer in the launch configuration the
+    benchmark uses; the oracle checks a seeded sample of lanes over every step."""
+    w = synth.WORKLOADS[name]
+    layer = w.layers - 1
+    n = 4 if w.L_dec <= 576 else 2
+    _, trace, stats = _parity(w, lanes=_sample_lanes(w, n, 7), layer=layer)
+    # every lane (not only the sample): selections at exactly t in [N_att-1, N_r-2], evictions t - (N_r - S)
+    T = w.L_dec
+    sel = trace[:, :, :, 0] >= 0
+    steps = np.arange(T)
+    want_sel = (steps >= w.N_att - 1) & (steps <= w.N_r - 2)
+    assert (sel == want_sel[:, None, None]).all()
+    want_ev = np.where(steps >= w.N_r, steps - (w.N_r - w.sink), -1)
+    assert (trace[:, :, :, 1] == want_ev[:, None, None]).all()
+    # choices are window positions: >= sink, <= t, inside the live window
+    ch = trace[:, :, :, 0]
+    tt = steps[:, None, None]
+    ok = ~sel | ((ch >= w.sink) & (ch <= tt) & (ch > tt - (w.N_r - w.sink)))
+    assert ok.all()
+
+
+def test_dense_full_size_janus7b_batch32_sampled():
+    w = synth.WORKLOADS["janus_pro_7b"].with_(batch=32)
+    T = w.L_dec
+    ins = device_inputs(w, 0, T, DEV)
+    out = run_dense(w, ins, T, DEV)
+    for (b, h) in _sample_lanes(w, 3, 11):
+        li = lane_inputs_from(w, 0, b, h, T)
+        ref = oracle.run_dense_lane(w.L_p, *li)
+        err = np.abs(out[:, b, h, :].cpu().numpy() - ref).max()
+        assert err <= tol(w), err
