@@ -41,7 +41,7 @@ enum Kind { KIND_SPARSE = 1, KIND_DENSE = 2 };
 struct dsa_state {
     int kind;
     int batch, heads, D, L_p, N_r, N_att, S, dtype, L_max;
-    int lanes, N_rw, N_attw;
+    int lanes, N_rw, N_attw, list_stride;
     long long lane_rows;
     char* ws;
     size_t ws_bytes;
@@ -57,6 +57,9 @@ struct dsa_state {
 namespace {
 
 size_t elem_size(int dtype) { return dtype == DSA_BF16 ? 2 : 4; }
+
+// Per-lane list entries, padded so every lane's list starts on 16 bytes.
+int list_stride_for(int n) { return (n + 7) / 8 * 8; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -102,13 +105,15 @@ int check_state(const dsa_state* st, int kind) {
     return 0;
 }
 
-// Wavefronts per workgroup: enough waves in flight over the whole chip
-// (256 CUs) while keeping a few rows per thread group.
+// Wavefronts per workgroup.  Measured on MI355X: the decode is fastest with
+// about 2-3 thousand wavefronts per launch in total (one workgroup per lane),
+// so lanes * waves is held near 3072, as long as every thread group keeps at
+// least the pipeline depth (4 rows) of work.
 int choose_waves(const dsa_state* st, long long rows) {
     if (st->waves) return st->waves;
     const int gpw = 64 / (st->D / (16 / (int)elem_size(st->dtype)));
     int w = 1;
-    while (w < 16 && (long long)st->lanes * w < 8192 && rows >= 4ll * gpw * (2 * w)) w *= 2;
+    while (w < 16 && (long long)st->lanes * (2 * w) <= 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;
     return w;
 }
 
@@ -129,7 +134,7 @@ int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
         a.B = st->batch;
         a.H = st->heads;
         a.L_p = st->L_p;
-        a.N_attw = st->N_attw;
+        a.list_stride = st->list_stride;
         hipError_t e = dsa::launch_prompt(st->dtype, st->D, a, st->stream);
         if (e != hipSuccess) return hip_fail(e, "prompt copy launch");
     }
@@ -181,7 +186,7 @@ size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int hea
     if (check_sparse(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype)) return 0;
     const long long lanes = (long long)batch * heads;
     return kv_bytes(lanes, (long long)L_p + N_r, head_dim, dtype) +
-           align_up((size_t)lanes * (size_t)(N_att - sink) * sizeof(int16_t));
+           align_up((size_t)lanes * (size_t)list_stride_for(N_att - sink) * sizeof(int16_t));
 }
 
 int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
@@ -207,6 +212,7 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->lanes = batch * heads;
     st->N_rw = N_r - sink;
     st->N_attw = N_att - sink;
+    st->list_stride = list_stride_for(N_att - sink);
     st->lane_rows = (long long)L_p + N_r;
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
@@ -249,6 +255,7 @@ int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) 
     a.S = S;
     a.N_rw = N_rw;
     a.N_attw = N_attw;
+    a.list_stride = st->list_stride;
     // Window entries attended at t: min(t' + 1, N_att') (phase 1 grows, then fixed).
     a.n_list = tw < 0 ? 0 : std::min(tw + 1, N_attw);
     a.n_sink = std::min(t + 1, S);
@@ -277,7 +284,7 @@ int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_
     if (h_offsets || h_count) {
         std::vector<int16_t> buf;
         try {
-            buf.resize((size_t)st->lanes * st->N_attw);
+            buf.resize((size_t)st->lanes * st->list_stride);
         } catch (...) {
             return fail(DSA_E_NOMEM, "host allocation failed");
         }
@@ -286,7 +293,7 @@ int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_
         e = hipMemcpy(buf.data(), st->ws + st->list_off, buf.size() * sizeof(int16_t), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_fail(e, "list copy");
         for (int l = 0; l < st->lanes; ++l) {
-            int16_t* src = buf.data() + (size_t)l * st->N_attw;
+            int16_t* src = buf.data() + (size_t)l * st->list_stride;
             std::sort(src, src + n);
             if (h_offsets) {
                 int16_t* dst = h_offsets + (size_t)l * st->N_attw;

@@ -14,7 +14,7 @@ enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1 };
 // resolved here once and the kernel only sees its consequences.
 struct DecodeArgs {
     const void* kv;        // cache base: [lanes][lane_rows][2][D] (K row then V row)
-    int16_t* list;         // sparse: [lanes][N_attw] attended window offsets (t - position)
+    int16_t* list;         // sparse: [lanes][list_stride] attended window offsets (t - position)
     const void* q;         // [lanes][D]
     const void* k_new;     // [lanes][D], the step's appended key
     const void* v_new;     // [lanes][D]
@@ -26,6 +26,7 @@ struct DecodeArgs {
     int S;                 // sink count (0 or 4)
     int N_rw;              // ring length for non-sink entries: N_r - S
     int N_attw;            // attended non-sink budget: N_att - S
+    int list_stride;       // entries per lane in the list: N_attw rounded up to 8 (16 bytes)
     int t;                 // decode step
     int n_list;            // sparse: entries of the list valid at this step
     int n_sink;            // sparse: sink positions attended at this step (min(t+1, S))
@@ -41,9 +42,9 @@ struct PromptArgs {
     const void* k_p;       // [B][L_p][H][D]
     const void* v_p;
     void* kv;
-    int16_t* list;         // nullable: when set, list[lane * N_attw] = 0 for every lane
+    int16_t* list;         // nullable: when set, list[lane * list_stride] = 0 for every lane
     long long lane_rows;
-    int B, H, L_p, N_attw;
+    int B, H, L_p, list_stride;
 };
 
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);

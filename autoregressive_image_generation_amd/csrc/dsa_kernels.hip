@@ -23,8 +23,11 @@ namespace dsa {
 namespace {
 
 constexpr int kMaxWaves = 16;
-constexpr int kMaxList = 8192;  // DSA_MAX_ATTEND
 constexpr float kNegBig = -1.0e30f;
+#ifndef DSA_ROWS_PER_CHUNK
+#define DSA_ROWS_PER_CHUNK 4
+#endif
+constexpr int kRowsPerChunk = DSA_ROWS_PER_CHUNK;  // pipeline depth in rows per thread group
 
 template <typename T>
 struct Traits;
@@ -55,6 +58,18 @@ __device__ __forceinline__ void unpack(const uint4& x, float* f) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Cache rows are read once per step and not again before every other layer
+// has streamed its own cache, so they bypass the caches' retention.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+#ifdef DSA_CACHED_ROWS
+    return *reinterpret_cast<const uint4*>(p);
+#else
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#endif
+}
 
 // Exchange a double with the lane a DPP pattern names (both halves moved).
 template <int CTRL>
@@ -101,14 +116,17 @@ __device__ __forceinline__ bool better(double s, int d, double bs, int bd) {
     return s < bs || (s == bs && d > bd);
 }
 
-template <typename T, int D, int MODE>
+// EARLY: every thread group's first U rows need no list entry (U * G <= number
+// of prompt + sink rows), so they are requested before the list has arrived.
+template <typename T, int D, int MODE, int U, bool EARLY>
 __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     constexpr int EPT = Traits<T>::EPT;
     constexpr int TPR = D / EPT;          // threads per half-row
     constexpr int GPW = 64 / TPR;         // thread groups per wavefront
     constexpr int ROW = 2 * D;            // elements per cache row
 
-    __shared__ int16_t s_list[MODE == MODE_SPARSE ? kMaxList : 1];
+    extern __shared__ uint4 s_list16[];   // sparse: the lane's attended offsets
+    int16_t* s_list = reinterpret_cast<int16_t*>(s_list16);
     __shared__ float s_m[kMaxWaves], s_l[kMaxWaves];
     __shared__ float s_acc[kMaxWaves][D];
     __shared__ double s_bs[kMaxWaves];
@@ -127,35 +145,80 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     const T* k_self = reinterpret_cast<const T*>(a.k_new) + (size_t)lane * D;
     const T* v_self = reinterpret_cast<const T*>(a.v_new) + (size_t)lane * D;
 
-    // Append: the new K/V row goes to its cache row.  Nothing this launch
-    // reads lives there (it is empty, or holds the entry evicted at this step);
-    // the current token itself is read from k_new / v_new.
-    {
-        constexpr int CH = ROW * (int)sizeof(T) / 16;
-        if (tid < CH) {
-            const int half = tid / (CH / 2);
-            const int c = tid % (CH / 2);
-            const T* src = (half ? v_self : k_self) + c * EPT;
-            T* dst = const_cast<T*>(lane_kv) + (size_t)(a.L_p + a.self_row) * ROW + half * D + c * EPT;
-            *reinterpret_cast<uint4*>(dst) = load16(src);
-        }
-    }
+    const int R = MODE == MODE_SPARSE ? a.L_p + a.n_sink + a.n_list : a.L_p + a.t + 1;
+    const int win0 = MODE == MODE_SPARSE ? a.L_p + a.n_sink : R;  // first listed row
+    constexpr int CH = ROW * (int)sizeof(T) / 16;                // 16-byte chunks per row
 
-    int R;
+    // Requests in the order their data is needed: the index list (16 bytes =
+    // 8 offsets per load; the list stride is padded to whole chunks), the
+    // query chunk, the appended row, then (EARLY) the first prompt rows.
+    // Vector loads complete in issue order, so waiting for the list only
+    // waits for what was issued before it.
+    const int nch = (a.n_list + 7) / 8;
+    const uint4* lst16 = reinterpret_cast<const uint4*>(a.list + (size_t)lane * a.list_stride);
+    uint4 lc0 = make_uint4(0, 0, 0, 0), lc1 = make_uint4(0, 0, 0, 0);
     if constexpr (MODE == MODE_SPARSE) {
-        const int16_t* lst = a.list + (size_t)lane * a.N_attw;
-        for (int j = tid; j < a.n_list; j += blockDim.x) s_list[j] = lst[j];
-        R = a.L_p + a.n_sink + a.n_list;
-        __syncthreads();
-    } else {
-        R = a.L_p + a.t + 1;
+        if (tid < nch) lc0 = load16(lst16 + tid);
+        if (tid + (int)blockDim.x < nch) lc1 = load16(lst16 + tid + blockDim.x);
     }
+    const uint4 qx = load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT);
+    uint4 ax = make_uint4(0, 0, 0, 0);
+    if (tid < CH) ax = load16((tid < CH / 2 ? k_self : v_self) + (tid % (CH / 2)) * EPT);
 
-    // The query chunk this thread multiplies, in fp64.
+    // Source of row r in [0, R): prompt rows, then sinks (sparse) or cached
+    // decode positions (dense) in their own cache rows, then the listed window
+    // entries: offset d = t - position, ring slot S + (t' - d) mod N_rw.  The
+    // current token is read from k_new / v_new.  Branch-free, so that the row
+    // loads below are straight-line code and every wait on them is exact.
+    auto row_src = [&](int r, const T*& kr, const T*& vr, int& d) {
+        const bool listed = r >= win0;
+        int dl = 0;
+        if constexpr (MODE == MODE_SPARSE) {
+            // Offsets are written only by this kernel and lie in [0, N_rw);
+            // the clamp keeps a damaged workspace from turning into stray reads.
+            dl = min(max((int)s_list[max(r - win0, 0)], 0), a.N_rw - 1);
+        }
+        int slot = a.base - dl;
+        slot += slot < 0 ? a.N_rw : 0;
+        const bool self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
+        const int row = listed ? a.L_p + a.S + slot : r;
+        const T* base = lane_kv + (size_t)row * ROW;
+        kr = self ? k_self : base;
+        vr = self ? v_self : base + D;
+        d = listed ? dl : -1;
+    };
+
+    // Rows of this group: r_k = g + k * G.  Every group of a wavefront runs the
+    // trip count of the wavefront's first group; rows past R re-read row R-1
+    // (cached) and are not consumed.
+    const int nk = (R - g + G - 1) / G;                      // rows this group consumes
+    const int nkw = (R - wave * GPW + G - 1) / G;             // trip count of the wavefront
+
+    uint4 kx[U], vx[U];
+    int dd[U];
+    auto first_rows = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const T* kr;
+            const T* vr;
+            row_src(min(g + u * G, R - 1), kr, vr, dd[u]);
+            kx[u] = load16_stream(kr + sl * EPT);
+            vx[u] = load16_stream(vr + sl * EPT);
+        }
+    };
+    if constexpr (EARLY) first_rows();  // prompt rows only: no list entry read
+    if constexpr (MODE == MODE_SPARSE) {
+        if (tid < nch) s_list16[tid] = lc0;
+        if (tid + (int)blockDim.x < nch) s_list16[tid + blockDim.x] = lc1;
+        for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_list16[c] = load16(lst16 + c);
+        __syncthreads();
+    }
+    if constexpr (!EARLY) first_rows();
+
     double qd[EPT];
     {
         float qf[EPT];
-        unpack<T>(load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT), qf);
+        unpack<T>(qx, qf);
 #pragma unroll
         for (int e = 0; e < EPT; ++e) qd[e] = (double)qf[e];
     }
@@ -167,88 +230,59 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     double best_s = __builtin_inf();
     int best_d = -1, best_j = -1;
 
-    const int win0 = a.L_p + a.n_sink;  // first window row (sparse)
+    // Consume one row: logit in fp64, argmin candidate, online softmax.  Rows
+    // past this group's share (k >= nk) enter with logit -inf and weight 0:
+    // selects instead of branches, so the loop below stays straight-line.
+    auto consume = [&](int k, const uint4& kq, const uint4& vq, int d) {
+        const bool valid = k < nk;
+        float kf[EPT], vf[EPT];
+        unpack<T>(kq, kf);
+        unpack<T>(vq, vf);
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
+        const double s = group_sum<TPR>(part);
+        if constexpr (MODE == MODE_SPARSE) {
+            const bool cand = valid && a.select && d >= 0 && better(s, d, best_s, best_d);
+            best_s = cand ? s : best_s;
+            best_d = cand ? d : best_d;
+            best_j = cand ? g + k * G - win0 : best_j;
+        }
+        const float x = valid ? (float)(s * a.scale_log2e) : -__builtin_inff();
+        const float mn = fmaxf(sm.m, x);
+        const float c = __builtin_amdgcn_exp2f(sm.m - mn);
+        const float p = __builtin_amdgcn_exp2f(x - mn);
+        sm.l = sm.l * c + p;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + p * vf[e];
+        sm.m = mn;
+    };
 
-    constexpr int U = 2;
-    for (int r0 = g; r0 < R; r0 += G * U) {
-        uint4 kx[U], vx[U];
-        int dd[U];
+    // Rolling pipeline: consume row k from its buffer, then refill that buffer
+    // with row k + U, so U - 1 rows stay in flight while one is computed.
+    int k0 = 0;
+    for (; k0 + U < nkw; k0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * G;
-            dd[u] = -1;
-            if (r < R) {
-                const T* kr;
-                const T* vr;
-                if (r < a.L_p) {
-                    kr = lane_kv + (size_t)r * ROW;
-                    vr = kr + D;
-                } else if constexpr (MODE == MODE_DENSE) {
-                    const int p = r - a.L_p;
-                    if (p == a.t) {
-                        kr = k_self;
-                        vr = v_self;
-                    } else {
-                        kr = lane_kv + (size_t)r * ROW;
-                        vr = kr + D;
-                    }
-                } else if (r < win0) {
-                    const int p = r - a.L_p;  // sink position = sink slot
-                    if (p == a.t) {
-                        kr = k_self;
-                        vr = v_self;
-                    } else {
-                        kr = lane_kv + (size_t)(a.L_p + p) * ROW;
-                        vr = kr + D;
-                    }
-                } else {
-                    // Offsets are written only by this kernel and lie in
-                    // [0, N_rw); the clamp keeps a damaged workspace from
-                    // turning into out-of-bounds reads.
-                    const int d = min(max((int)s_list[r - win0], 0), a.N_rw - 1);
-                    dd[u] = d;
-                    if (d == 0) {
-                        kr = k_self;
-                        vr = v_self;
-                    } else {
-                        int slot = a.base - d;
-                        if (slot < 0) slot += a.N_rw;
-                        kr = lane_kv + (size_t)(a.L_p + a.S + slot) * ROW;
-                        vr = kr + D;
-                    }
-                }
-                kx[u] = load16(kr + sl * EPT);
-                vx[u] = load16(vr + sl * EPT);
-            }
+            consume(k0 + u, kx[u], vx[u], dd[u]);
+            const T* kr;
+            const T* vr;
+            row_src(min(g + (k0 + u + U) * G, R - 1), kr, vr, dd[u]);
+            kx[u] = load16_stream(kr + sl * EPT);
+            vx[u] = load16_stream(vr + sl * EPT);
         }
+    }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * G;
-            if (r < R) {
-                float kf[EPT], vf[EPT];
-                unpack<T>(kx[u], kf);
-                unpack<T>(vx[u], vf);
-                double part = 0.0;
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
-                const double s = group_sum<TPR>(part);
-                if constexpr (MODE == MODE_SPARSE) {
-                    if (a.select && dd[u] >= 0 && better(s, dd[u], best_s, best_d)) {
-                        best_s = s;
-                        best_d = dd[u];
-                        best_j = r - win0;
-                    }
-                }
-                const float x = (float)(s * a.scale_log2e);
-                const float mn = fmaxf(sm.m, x);
-                const float c = __builtin_amdgcn_exp2f(sm.m - mn);
-                const float p = __builtin_amdgcn_exp2f(x - mn);
-                sm.l = sm.l * c + p;
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + p * vf[e];
-                sm.m = mn;
-            }
-        }
+    for (int u = 0; u < U; ++u) consume(k0 + u, kx[u], vx[u], dd[u]);
+
+    // Append: the new K/V row goes to its cache row.  Nothing this launch
+    // reads lives there (it is empty, or holds the entry evicted at this step);
+    // the current token itself is read from k_new / v_new.  Loaded at the
+    // start, stored here, so it adds no latency of its own.
+    if (tid < CH) {
+        T* dst = const_cast<T*>(lane_kv) + (size_t)(a.L_p + a.self_row) * ROW + (tid / (CH / 2)) * D +
+                 (tid % (CH / 2)) * EPT;
+        *reinterpret_cast<uint4*>(dst) = ax;
     }
 
     // Merge the groups of this wavefront (butterfly over lanes TPR apart).
@@ -308,7 +342,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
                 best_j = s_bj[w];
             }
         }
-        int16_t* lst = a.list + (size_t)lane * a.N_attw;
+        int16_t* lst = a.list + (size_t)lane * a.list_stride;
         int chosen = -1;
         if (a.select) {
             // skip_idx.append(idx[j*]): offset best_d leaves the attended list
@@ -352,17 +386,25 @@ __global__ void prompt_kernel(PromptArgs a) {
     if (a.list) {
         const int lanes = a.B * a.H;
         for (int l = blockIdx.x * blockDim.x + threadIdx.x; l < lanes; l += gridDim.x * blockDim.x)
-            a.list[(size_t)l * a.N_attw] = 0;
+            a.list[(size_t)l * a.list_stride] = 0;
     }
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
+    constexpr int U = kRowsPerChunk;
+    constexpr int TPR = D / Traits<T>::EPT;
+    const int G = waves * (64 / TPR);
     dim3 grid(a.lanes), block(64 * waves);
-    if (mode == MODE_SPARSE)
-        hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, D, MODE_DENSE>), grid, block, 0, s, a);
+    if (mode == MODE_SPARSE) {
+        const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;
+        if (U * G <= a.L_p + a.n_sink)
+            hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
+    } else {
+        hipLaunchKernelGGL((decode_kernel<T, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

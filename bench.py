@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB 5 times (HBM counter calibration) and exit")
     return p.parse_args()
 
 
@@ -323,6 +325,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"calibrate_copy_bytes": n, "reads": n, "writes": n, "launches": 5}), flush=True)
+        return
 
     w = synth.WORKLOADS[args.workload]
     layers = args.layers or w.layers

@@ -52,7 +52,8 @@ def _align(x):
 def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
     es = 2 if dt == 1 else 4
     lanes = B * H
-    want = _align(lanes * (L_p + N_r) * 2 * D * es) + _align(lanes * (N_att - S) * 2)
+    stride = (N_att - S + 7) // 8 * 8      # per-lane list padded to 16 bytes
+    want = _align(lanes * (L_p + N_r) * 2 * D * es) + _align(lanes * stride * 2)
     assert dsa.dsa_state_workspace_bytes(B, L_p, N_r, N_att, H, D, S, dt) == want
     assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * 2 * D * es)
 
