@@ -27,6 +27,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 
+# HBM bytes per sparse-decode launch from rocprofv3 counters, filled in from
+# the committed profiles (FETCH_SIZE + WRITE_SIZE, each scaled by the factor a
+# plain copy of known size gives); None until measured for a workload.
+TRAFFIC = {}
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -346,15 +351,23 @@ def main():
     total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
     log("sparse: %.1f ms per decode (events %.1f ms)" % (sec * 1e3, sec_ev * 1e3))
 
-    # roofline of the sparse kernel from per-launch events
-    durs = kernel_durations(sparse, layers, dev)
-    lane_count = w.batch * w.heads
-    kb = sum(sparse_bytes_per_head_step(w, t) * lane_count * layers for t in range(w.L_dec))
-    kt = sum(sum(d) for d in durs)
+    # Roofline of the sparse kernel from the timed region's HIP events (torch's
+    # current stream is the stream the library launches on): the launches run
+    # back to back, so events / launches is the average launch duration,
+    # inter-launch gaps included (rocprofv3's kernel trace agrees within ~1 %).
     n_launch = w.L_dec * layers
-    achieved = kb / kt / 1e9
-    phase3 = [sum(durs[t]) / layers for t in range(w.N_r, w.L_dec)] if w.L_dec > w.N_r else []
-    log("sparse kernel: %.2f us avg over %d launches, %.0f GB/s" % (kt / n_launch * 1e6, n_launch, achieved))
+    launch_s = sec_ev / n_launch
+    bytes_per_launch = total_bytes / n_launch
+    achieved = bytes_per_launch / launch_s / 1e9
+    log("sparse kernel: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
+    # per-phase latency from one decode with an event pair around every launch
+    # (each pair adds ~2 us of event overhead; for the step profile only)
+    durs = kernel_durations(sparse, layers, dev)
+    phase_us = {}
+    for name, lo, hi in (("phase1", 0, min(w.N_att - 1, w.L_dec)), ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
+                         ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
+        if hi > lo:
+            phase_us[name] = sum(sum(durs[t]) for t in range(lo, hi)) / ((hi - lo) * layers) * 1e6
 
     result = {
         "metric": "sparse decode-attn steps/s (batch x layers x heads) + HBM GB/s, Janus-Pro-7B shape",
@@ -376,11 +389,11 @@ def main():
                    "accumulation": "fp64 logits, fp32 softmax and PV"},
         "hbm_gbs": total_bytes / sec / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_kernel<bf16,128,sparse>",
-                     "avg_launch_us": kt / n_launch * 1e6,
-                     "bytes_per_launch": kb / n_launch,
-                     "phase3_avg_launch_us": (sum(phase3) / len(phase3) * 1e6) if phase3 else None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": TRAFFIC.get(w.name),
+                     "kernel": "decode_kernel (sparse, bf16, head_dim 128)",
+                     "avg_launch_us": launch_s * 1e6,
+                     "bytes_per_launch": bytes_per_launch,
+                     "event_pair_us_by_phase": phase_us},
         "events_ms_per_step": sec_ev * 1e3,
     }
 
