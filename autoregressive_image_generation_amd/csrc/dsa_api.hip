@@ -106,14 +106,15 @@ int check_state(const dsa_state* st, int kind) {
 }
 
 // Wavefronts per workgroup.  Measured on MI355X: the decode is fastest with
-// about 2-3 thousand wavefronts per launch in total (one workgroup per lane),
-// so lanes * waves is held near 3072, as long as every thread group keeps at
-// least the pipeline depth (4 rows) of work.
+// one to three thousand wavefronts per launch in total (one workgroup per
+// lane), so waves doubles while lanes * waves stays below 3072, every thread
+// group keeps at least the pipeline depth (4 rows) of work, and the workgroup
+// stays at 8 wavefronts or fewer (16 was slower at every measured shape).
 int choose_waves(const dsa_state* st, long long rows) {
     if (st->waves) return st->waves;
     const int gpw = 64 / (st->D / (16 / (int)elem_size(st->dtype)));
     int w = 1;
-    while (w < 16 && (long long)st->lanes * (2 * w) <= 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;
+    while (w < 8 && (long long)st->lanes * (2 * w) < 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;
     return w;
 }
 

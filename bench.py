@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--workload", default="janus_pro_7b")
     p.add_argument("--dense-batch", type=int, default=32, help="batch of the dense comparison (0: skip)")
     p.add_argument("--waves", type=int, default=0, help="wavefronts per lane (0: library's choice)")
+    p.add_argument("--streams", type=int, default=0,
+                   help="micro-batches, each on its own stream (0: 2 when the batch is even, else 1)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
@@ -134,108 +136,154 @@ class Inputs:
 
 
 # ----------------------------------------------------------------------------- runs
-class SparseModel:
-    """One sparse state per layer over caller-owned workspaces."""
+# Wavefronts per lane measured best on MI355X with two micro-batch streams
+# (full 30/32-layer loops; 0 = the library's own choice).
+MEASURED_WAVES = {"janus_pro_7b": 1, "janus_pro_1b": 4, "lumina_mgpt_7b_1024": 4, "hires_8100_sink4": 8}
 
-    def __init__(self, w, inputs, layers, dev, waves, batch=None):
+_STREAM_POOL = []
+
+
+def micro_batch_streams(dev, n):
+    """The process's micro-batch streams (default priority), created once and
+    shared by every model.  Creating streams per model made every other model's
+    pair share one hardware queue (GPU_MAX_HW_QUEUES = 4), which serialises it."""
+    import torch
+
+    while len(_STREAM_POOL) < n:
+        _STREAM_POOL.append(torch.cuda.Stream(dev))
+    return _STREAM_POOL[:n]
+
+
+class SparseModel:
+    """One sparse state per layer over caller-owned workspaces.
+
+    With streams > 1 the batch is split into that many micro-batches, each with
+    its own per-layer states on its own stream (default priority).  Every
+    sequence still goes through the layers in model order; micro-batches are
+    independent, so one's launch can overlap another's.
+    """
+
+    def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1):
         import torch
 
         import autoregressive_image_generation_amd as dsa
 
         self.dsa, self.w, self.inputs, self.dev = dsa, w, inputs, dev
         self.B = batch or w.batch
-        self.nbytes = dsa.dsa_state_workspace_bytes(self.B, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink,
+        if self.B % streams:
+            raise ValueError("batch %d does not split into %d micro-batches" % (self.B, streams))
+        self.S = streams
+        self.Bc = self.B // streams
+        self.nbytes = dsa.dsa_state_workspace_bytes(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink,
                                                     w.dtype)
-        self.ws = [torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
+        self.ws = [[torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
+                   for _ in range(streams)]
         self.out = torch.empty((self.B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+        self.streams = [torch.cuda.current_stream(dev)] if streams == 1 else micro_batch_streams(dev, streams)
         self.waves = waves
-        self.states = []
+        self.states = []  # [micro-batch][layer]
+
+    def _init_state(self, ws, stream):
+        w = self.w
+        return self.dsa.dsa_state_init(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink, w.dtype, ws,
+                                       self.nbytes, stream)
+
+    def _append_prompt(self, st, x, c):
+        w = self.w
+        off = c * self.Bc * w.L_p * w.heads * w.head_dim * x["kp"].element_size()
+        self.dsa.dsa_append_prompt(st, x["kp"].data_ptr() + off if w.L_p else None,
+                                   x["vp"].data_ptr() + off if w.L_p else None)
 
     def reset(self):
         """Fresh states with the prompt in the cache (the prefill's part; not timed)."""
         import torch
 
-        dsa, w = self.dsa, self.w
-        for st in self.states:
-            dsa.dsa_state_destroy(st)
+        dsa = self.dsa
+        for row in self.states:
+            for st in row:
+                dsa.dsa_state_destroy(st)
         self.states = []
-        stream = torch.cuda.current_stream(self.dev)
-        for layer, ws in enumerate(self.ws):
-            st = dsa.dsa_state_init(self.B, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink, w.dtype, ws,
-                                    self.nbytes, stream)
-            dsa.dsa_set_waves(st, self.waves)
-            x = self.inputs.layers[layer]
-            dsa.dsa_append_prompt(st, x["kp"] if w.L_p else None, x["vp"] if w.L_p else None)
-            self.states.append(st)
+        torch.cuda.synchronize(self.dev)
+        for c in range(self.S):
+            row = []
+            for layer, ws in enumerate(self.ws[c]):
+                st = self._init_state(ws, self.streams[c])
+                dsa.dsa_set_waves(st, self.waves)
+                self._append_prompt(st, self.inputs.layers[layer], c)
+                row.append(st)
+            self.states.append(row)
         torch.cuda.synchronize(self.dev)
 
+    def _decode_fn(self):
+        return self.dsa.library().dsa_decode_step
+
     def decode(self):
-        """All L_dec steps through all layers, in model order."""
+        """All L_dec steps through all layers, in model order per micro-batch."""
         dsa, w = self.dsa, self.w
         q0 = self.inputs.layers[0]["q"]
-        step_bytes = q0[0].numel() * q0.element_size()
+        es = q0.element_size()
+        step_bytes = q0[0].numel() * es
+        chunk = self.Bc * w.heads * w.head_dim
         ptrs = [(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr()) for x in self.inputs.layers]
         lib = dsa.library()
-        out = self.out.data_ptr()
+        append = lib.dsa_append_kv if not isinstance(self, DenseModel) else lib.dense_append_kv
+        outs = [self.out.data_ptr() + c * chunk * 4 for c in range(self.S)]
+        layers = len(ptrs)
+        dense = isinstance(self, DenseModel)
         for t in range(w.L_dec):
-            off = t * step_bytes  # step t's first `B` sequences are contiguous in [B][H][D]
-            for st, (qp, kp, vp) in zip(self.states, ptrs):
-                rc = lib.dsa_append_kv(st, kp + off, vp + off)
-                rc |= lib.dsa_decode_step(st, qp + off, out, None)
-                if rc:
-                    raise dsa.DsaError(rc, dsa.dsa_last_error())
+            for layer in range(layers):
+                qp, kp, vp = ptrs[layer]
+                for c in range(self.S):
+                    off = t * step_bytes + c * chunk * es  # micro-batch c of step t: contiguous in [B][H][D]
+                    st = self.states[c][layer]
+                    rc = append(st, kp + off, vp + off)
+                    if dense:
+                        rc |= lib.dense_decode_step(st, qp + off, outs[c])
+                    else:
+                        rc |= lib.dsa_decode_step(st, qp + off, outs[c], None)
+                    if rc:
+                        raise dsa.DsaError(rc, dsa.dsa_last_error())
 
 
 class DenseModel(SparseModel):
-    def __init__(self, w, inputs, layers, dev, waves, batch):
+    """One dense state per layer (optionally per micro-batch and stream)."""
+
+    def __init__(self, w, inputs, layers, dev, waves, batch, streams=1):
         import torch
 
         import autoregressive_image_generation_amd as dsa
 
         self.dsa, self.w, self.inputs, self.dev = dsa, w, inputs, dev
         self.B = batch
-        self.nbytes = dsa.dense_state_workspace_bytes(batch, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype)
-        self.ws = [torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
+        if self.B % streams:
+            raise ValueError("batch %d does not split into %d micro-batches" % (self.B, streams))
+        self.S = streams
+        self.Bc = self.B // streams
+        self.nbytes = dsa.dense_state_workspace_bytes(self.Bc, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype)
+        self.ws = [[torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
+                   for _ in range(streams)]
         self.out = torch.empty((batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+        self.streams = [torch.cuda.current_stream(dev)] if streams == 1 else micro_batch_streams(dev, streams)
         self.waves = waves
         self.states = []
 
-    def reset(self):
-        import torch
+    def _init_state(self, ws, stream):
+        w = self.w
+        return self.dsa.dense_state_init(self.Bc, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype, ws, self.nbytes,
+                                         stream)
 
-        dsa, w = self.dsa, self.w
-        for st in self.states:
-            dsa.dsa_state_destroy(st)
-        self.states = []
-        stream = torch.cuda.current_stream(self.dev)
-        for layer, ws in enumerate(self.ws):
-            st = dsa.dense_state_init(self.B, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype, ws, self.nbytes, stream)
-            dsa.dsa_set_waves(st, self.waves)
-            x = self.inputs.layers[layer]
-            # the first `batch` sequences of the prompt: [B][L_p][H][D] keeps them contiguous
-            dsa.dense_append_prompt(st, x["kp"] if w.L_p else None, x["vp"] if w.L_p else None)
-            self.states.append(st)
-        torch.cuda.synchronize(self.dev)
-
-    def decode(self):
-        dsa, w = self.dsa, self.w
-        q0 = self.inputs.layers[0]["q"]
-        step_bytes = q0[0].numel() * q0.element_size()
-        ptrs = [(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr()) for x in self.inputs.layers]
-        lib = dsa.library()
-        out = self.out.data_ptr()
-        for t in range(w.L_dec):
-            off = t * step_bytes  # step t's first `batch` sequences are contiguous in [B][H][D]
-            for st, (qp, kp, vp) in zip(self.states, ptrs):
-                rc = lib.dense_append_kv(st, kp + off, vp + off)
-                rc |= lib.dense_decode_step(st, qp + off, out)
-                if rc:
-                    raise dsa.DsaError(rc, dsa.dsa_last_error())
+    def _append_prompt(self, st, x, c):
+        w = self.w
+        off = c * self.Bc * w.L_p * w.heads * w.head_dim * x["kp"].element_size()
+        self.dsa.dense_append_prompt(st, x["kp"].data_ptr() + off if w.L_p else None,
+                                     x["vp"].data_ptr() + off if w.L_p else None)
 
 
 def time_decodes(model, steps, warmup, dev):
     """Warm-up decodes, then `steps` timed decodes, each bracketed by a device
-    synchronisation; returns (seconds per decode by host clock, by HIP events)."""
+    synchronisation; returns (seconds per decode by host clock, by HIP events).
+    The events sit on the launch stream(s): with several micro-batch streams,
+    every stream waits for the start event and the stop event waits for all."""
     import torch
 
     for _ in range(warmup):
@@ -243,17 +291,30 @@ def time_decodes(model, steps, warmup, dev):
         model.decode()
     torch.cuda.synchronize(dev)
     wall = ev = 0.0
+    per_stream = [0.0] * len(model.streams)
+    main = torch.cuda.current_stream(dev)
     for _ in range(steps):
         model.reset()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ends = [torch.cuda.Event(enable_timing=True) for _ in model.streams]
         torch.cuda.synchronize(dev)
         t0 = time.perf_counter()
-        start.record()
+        start.record(main)
+        for s in model.streams:
+            if s != main:
+                s.wait_event(start)
         model.decode()
-        stop.record()
+        for s, e in zip(model.streams, ends):
+            e.record(s)
+            if s != main:
+                main.wait_event(e)
+        stop.record(main)
         torch.cuda.synchronize(dev)
         wall += time.perf_counter() - t0
         ev += start.elapsed_time(stop) * 1e-3
+        for i, e in enumerate(ends):
+            per_stream[i] += start.elapsed_time(e) * 1e-3
+    model.stream_seconds = [x / steps for x in per_stream]
     return wall / steps, ev / steps
 
 
@@ -263,6 +324,8 @@ def kernel_durations(model, layers, dev):
     launch durations in seconds."""
     import torch
 
+    if model.S != 1:
+        return None
     model.reset()
     w = model.w
     n = w.L_dec * layers
@@ -275,7 +338,7 @@ def kernel_durations(model, layers, dev):
     i = 0
     for t in range(w.L_dec):
         off = t * step_bytes
-        for st, (qp, kp, vp) in zip(model.states, ptrs):
+        for st, (qp, kp, vp) in zip(model.states[0], ptrs):
             rc = lib.dsa_append_kv(st, kp + off, vp + off)
             evs[2 * i].record()
             rc |= lib.dsa_decode_step(st, qp + off, out, None)
@@ -367,25 +430,30 @@ def main():
     log("inputs ready in %.1f s" % inputs.gen_seconds)
 
     head_steps = w.batch * layers * w.heads * w.L_dec
-    sparse = SparseModel(w, inputs, layers, dev, args.waves)
+    S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
+    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    sparse = SparseModel(w, inputs, layers, dev, waves, streams=S)
     sec, sec_ev = time_decodes(sparse, args.steps, args.warmup, dev)
     total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
-    log("sparse: %.1f ms per decode (events %.1f ms)" % (sec * 1e3, sec_ev * 1e3))
+    log("sparse (%d micro-batch streams): %.1f ms per decode (events %.1f ms)" % (S, sec * 1e3, sec_ev * 1e3))
 
-    # Roofline of the sparse kernel from the timed region's HIP events (torch's
-    # current stream is the stream the library launches on): the launches run
-    # back to back, so events / launches is the average launch duration,
-    # inter-launch gaps included (rocprofv3's kernel trace agrees within ~1 %).
-    n_launch = w.L_dec * layers
-    launch_s = sec_ev / n_launch
-    bytes_per_launch = total_bytes / n_launch
-    achieved = bytes_per_launch / launch_s / 1e9
-    log("sparse kernel: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
+    # Roofline of the sparse kernel from the timed region's HIP events, recorded
+    # on the stream(s) the library launches on.  Each stream's launches run back
+    # to back, so a stream's event time / its launches is that kernel's average
+    # launch duration, gaps included (what rocprofv3's kernel trace reports per
+    # dispatch).  With S micro-batch streams, S such launches run at once; the
+    # achieved bandwidth is the sum over streams = all algorithmic bytes / time.
+    n_launch = w.L_dec * layers                      # launches per stream
+    launch_s = sum(sparse.stream_seconds) / S / n_launch
+    bytes_per_launch = total_bytes / n_launch / S    # one micro-batch's kernel
+    achieved = total_bytes / sec_ev / 1e9
+    log("sparse kernel: %.2f us per launch per stream, %d streams x %d launches, %.0f GB/s"
+        % (launch_s * 1e6, S, n_launch, achieved))
     # per-phase latency from one decode with an event pair around every launch
     # (each pair adds ~2 us of event overhead; for the step profile only)
     durs = kernel_durations(sparse, layers, dev)
     phase_us = {}
-    for name, lo, hi in (("phase1", 0, min(w.N_att - 1, w.L_dec)), ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
+    for name, lo, hi in [] if durs is None else (("phase1", 0, min(w.N_att - 1, w.L_dec)), ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
                          ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
         if hi > lo:
             phase_us[name] = sum(sum(durs[t]) for t in range(lo, hi)) / ((hi - lo) * layers) * 1e6
@@ -407,6 +475,8 @@ def main():
                    "head_dim": w.head_dim, "L_p": w.L_p, "L_dec": w.L_dec, "N_r": w.N_r, "N_att": w.N_att,
                    "sink": w.sink, "sparsity": round(1 - w.N_att / w.L_dec, 4),
                    "step": "one full image decode: L_dec tokens x layers, all lanes",
+                   "micro_batches": S,
+                   "waves_per_lane": waves or "library choice",
                    "accumulation": "fp64 logits, fp32 softmax and PV"},
         "hbm_gbs": total_bytes / sec / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -414,19 +484,32 @@ def main():
                      "kernel": "decode_kernel (sparse, bf16, head_dim 128)",
                      "avg_launch_us": launch_s * 1e6,
                      "bytes_per_launch": bytes_per_launch,
+                     "concurrent_streams": S,
                      "event_pair_us_by_phase": phase_us},
         "events_ms_per_step": sec_ev * 1e3,
     }
 
+    if S > 1:
+        # the same decode on one stream, for reference
+        single = SparseModel(w, inputs, layers, dev, args.waves, streams=1)
+        s1, s1_ev = time_decodes(single, args.steps, args.warmup, dev)
+        result["single_stream"] = {"value": head_steps / s1, "ms_per_step": s1 * 1e3,
+                                   "achieved_gbs": total_bytes / s1_ev / 1e9,
+                                   "avg_launch_us": s1_ev / n_launch * 1e6}
+        log("sparse, one stream: %.1f ms per decode" % (s1 * 1e3))
+        del single
+
     if args.dense_batch:
         db = min(args.dense_batch, w.batch)
-        dense = DenseModel(w, inputs, layers, dev, args.waves, db)
+        dS = S if db % S == 0 else 1
+        dense = DenseModel(w, inputs, layers, dev, args.waves, db, streams=dS)
         dsec, _ = time_decodes(dense, args.steps, args.warmup, dev)
         dsteps = db * layers * w.heads * w.L_dec
         dbytes = sum(dense_bytes_per_head_step(w, t) for t in range(w.L_dec)) * db * w.heads * layers
-        sparse_b = SparseModel(w, inputs, layers, dev, args.waves, batch=db)
+        sparse_b = SparseModel(w, inputs, layers, dev, args.waves, batch=db, streams=dS)
         ssec, _ = time_decodes(sparse_b, args.steps, args.warmup, dev)
-        result["dense"] = {"batch": db, "value": dsteps / dsec, "unit": "head-steps/s", "hbm_gbs": dbytes / dsec / 1e9,
+        result["dense"] = {"batch": db, "micro_batches": dS, "value": dsteps / dsec, "unit": "head-steps/s",
+                           "hbm_gbs": dbytes / dsec / 1e9,
                            "ms_per_step": dsec * 1e3, "sparse_same_batch_value": dsteps / ssec,
                            "sparse_speedup": dsec / ssec,
                            "byte_ratio": dbytes / (sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec))
@@ -441,7 +524,7 @@ def main():
             n_att = synth.n_att_for(w.L_dec, sp)
             n_r = w.N_r if n_att <= w.N_r else w.L_dec
             ws = w.with_(N_att=n_att, N_r=n_r)
-            m = SparseModel(ws, inputs, layers, dev, args.waves)
+            m = SparseModel(ws, inputs, layers, dev, args.waves, streams=S)
             s, _ = time_decodes(m, 1, 1, dev)
             b = sum(sparse_bytes_per_head_step(ws, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
             sweep.append({"sparsity": sp, "N_r": n_r, "N_att": n_att, "value": head_steps / s,
