@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
+    p.add_argument("--summarize-trace", metavar="CSV",
+                   help="only summarise a rocprofv3 run_kernel_trace.csv by kernel and launch shape, then exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 5 times (HBM counter calibration) and exit")
     return p.parse_args()
@@ -393,8 +395,42 @@ def cpu_baseline(w, target_cpu_seconds):
                       % (n, T, w.name, wall, wall * threads, probe)}
 
 
+def summarize_trace(path):
+    """Per kernel and launch shape: dispatches and mean / min / max duration,
+    plus the busy time (union of dispatch intervals) of each launch shape."""
+    import csv
+    from collections import defaultdict
+
+    groups = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups[key].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows = []
+    for (name, grid, wg), iv in sorted(groups.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        d = [e - s for s, e in iv]
+        iv.sort()
+        busy, cur_s, cur_e = 0, None, None
+        for s0, e0 in iv:
+            if cur_e is None or s0 > cur_e:
+                if cur_e is not None:
+                    busy += cur_e - cur_s
+                cur_s, cur_e = s0, e0
+            else:
+                cur_e = max(cur_e, e0)
+        busy += cur_e - cur_s
+        rows.append({"kernel": name, "grid": grid, "workgroup": wg, "dispatches": len(d),
+                     "mean_us": sum(d) / len(d) / 1e3, "min_us": min(d) / 1e3, "max_us": max(d) / 1e3,
+                     "busy_us_per_dispatch": busy / len(d) / 1e3})
+    for r in rows:
+        print(json.dumps(r))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (lanes shard across GPUs "
               "with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
