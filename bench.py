@@ -33,9 +33,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 # profiles/ summaries give the commands.  Keyed by workload and tied to the
 # kernel source it was measured on: reported as null once that source changes.
 TRAFFIC = {
-    "janus_pro_7b": {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "5ebed0da750676a7",
-                     "launches": "sparse decode dispatches 12000-12299 (steps 400-409, phase 3)",
-                     "algorithmic_bytes_same_launches": 150386688},
+    # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
+    # algorithmic bytes of the same launches 150386688
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "5ebed0da750676a7"},
+    # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.5e6, "kernel_sha256_16": "5ebed0da750676a7"},
 }
 
 
@@ -47,8 +49,8 @@ def kernel_sha16():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(name):
-    t = TRAFFIC.get(name)
+def traffic_for(name, streams=1):
+    t = TRAFFIC.get((name, streams))
     if not t or t["kernel_sha256_16"] != kernel_sha16():
         return None
     return t["bytes_per_launch"]
@@ -468,29 +470,41 @@ def main():
     head_steps = w.batch * layers * w.heads * w.L_dec
     S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
     waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+    n_launch = w.L_dec * layers  # launches per stream
+
+    # The whole job: the decode split into S micro-batches on S streams.
     sparse = SparseModel(w, inputs, layers, dev, waves, streams=S)
     sec, sec_ev = time_decodes(sparse, args.steps, args.warmup, dev)
-    total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
     log("sparse (%d micro-batch streams): %.1f ms per decode (events %.1f ms)" % (S, sec * 1e3, sec_ev * 1e3))
+    per_stream_launch_s = sum(sparse.stream_seconds) / S / n_launch
 
-    # Roofline of the sparse kernel from the timed region's HIP events, recorded
-    # on the stream(s) the library launches on.  Each stream's launches run back
-    # to back, so a stream's event time / its launches is that kernel's average
-    # launch duration, gaps included (what rocprofv3's kernel trace reports per
-    # dispatch).  With S micro-batch streams, S such launches run at once; the
-    # achieved bandwidth is the sum over streams = all algorithmic bytes / time.
-    n_launch = w.L_dec * layers                      # launches per stream
-    launch_s = sum(sparse.stream_seconds) / S / n_launch
-    bytes_per_launch = total_bytes / n_launch / S    # one micro-batch's kernel
-    achieved = total_bytes / sec_ev / 1e9
-    log("sparse kernel: %.2f us per launch per stream, %d streams x %d launches, %.0f GB/s"
-        % (launch_s * 1e6, S, n_launch, achieved))
+    # The kernel alone: the same decode on one stream.  Its launches run back
+    # to back, so the timed region's HIP events (recorded on the stream the
+    # library launches on) / the launches is the kernel's average launch
+    # duration, gaps included, which is what rocprofv3's kernel trace reports
+    # per dispatch.  With S streams, S launches overlap; the kernel trace
+    # cannot follow that (the profiler serialises much of the overlap), so the
+    # aggregate over streams is reported apart.
+    if S > 1:
+        del sparse
+        single = SparseModel(w, inputs, layers, dev, args.waves, streams=1)
+        s1, s1_ev = time_decodes(single, args.steps, args.warmup, dev)
+        log("sparse, one stream: %.1f ms per decode" % (s1 * 1e3))
+    else:
+        single, s1, s1_ev = sparse, sec, sec_ev
+    launch_s = s1_ev / n_launch
+    bytes_per_launch = total_bytes / n_launch
+    achieved = bytes_per_launch / launch_s / 1e9
+    log("sparse kernel alone: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
     # per-phase latency from one decode with an event pair around every launch
     # (each pair adds ~2 us of event overhead; for the step profile only)
-    durs = kernel_durations(sparse, layers, dev)
+    durs = kernel_durations(single, layers, dev)
+    del single
     phase_us = {}
-    for name, lo, hi in [] if durs is None else (("phase1", 0, min(w.N_att - 1, w.L_dec)), ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
-                         ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
+    for name, lo, hi in [] if durs is None else (("phase1", 0, min(w.N_att - 1, w.L_dec)),
+                                                 ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
+                                                 ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
         if hi > lo:
             phase_us[name] = sum(sum(durs[t]) for t in range(lo, hi)) / ((hi - lo) * layers) * 1e6
 
@@ -517,23 +531,21 @@ def main():
         "hbm_gbs": total_bytes / sec / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(w.name),
-                     "kernel": "decode_kernel (sparse, bf16, head_dim 128)",
+                     "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
                      "avg_launch_us": launch_s * 1e6,
                      "bytes_per_launch": bytes_per_launch,
-                     "concurrent_streams": S,
                      "event_pair_us_by_phase": phase_us},
         "events_ms_per_step": sec_ev * 1e3,
     }
-
     if S > 1:
-        # the same decode on one stream, for reference
-        single = SparseModel(w, inputs, layers, dev, args.waves, streams=1)
-        s1, s1_ev = time_decodes(single, args.steps, args.warmup, dev)
-        result["single_stream"] = {"value": head_steps / s1, "ms_per_step": s1 * 1e3,
-                                   "achieved_gbs": total_bytes / s1_ev / 1e9,
-                                   "avg_launch_us": s1_ev / n_launch * 1e6}
-        log("sparse, one stream: %.1f ms per decode" % (s1 * 1e3))
-        del single
+        agg = total_bytes / sec_ev / 1e9
+        result["roofline_micro_batched"] = {
+            "achieved": agg, "frac": agg / HBM_PEAK_GBS, "unit": "GB/s", "streams": S,
+            "traffic": traffic_for(w.name, S),
+            "avg_launch_us_per_stream": per_stream_launch_s * 1e6,
+            "bytes_per_launch": total_bytes / n_launch / S,
+            "note": "S launches of one micro-batch each in flight at once; all algorithmic bytes / event time"}
+        result["single_stream"] = {"value": head_steps / s1, "ms_per_step": s1 * 1e3}
 
     if args.dense_batch:
         db = min(args.dense_batch, w.batch)
