@@ -1,14 +1,15 @@
-"""CPU oracle for diagonal-aware sparse decode attention (fp64).
+"""CPU oracle for diagonal-aware sparse decode attention and its baselines (fp64).
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
-the GPU library.  The algorithm itself lives in ``dsa_oracle.c`` (Algorithm 1
-of "Understanding and Exploiting Diagonal Attention Sparsity in Autoregressive
-Image Generation", Section 4); this module compiles it with gcc and marshals
-numpy arrays.
+the GPU library.  The algorithms live in C: ``dsa_oracle.c`` (Algorithm 1 of
+"Understanding and Exploiting Diagonal Attention Sparsity in Autoregressive
+Image Generation", Section 4, and the dense step) and ``baselines_oracle.c``
+(SlidingWindow, StreamingLLM, TOVA and H2O as Sections 2.3 and 5.1 describe
+them); this module compiles them with gcc and marshals numpy arrays.
 
-Every function here is pinned by ``tests/test_oracle_*.py``; none is "parity
-unpinned".
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_baselines.py``; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -19,16 +20,16 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_SRCS = [os.path.join(_HERE, "dsa_oracle.c"), os.path.join(_HERE, "baselines_oracle.c")]
 _LIB = os.path.join(_HERE, "_liboracle.so")
 
 _P = ctypes.c_void_p
 
 
 def build() -> str:
-    """Compile dsa_oracle.c into _liboracle.so (always recompiles)."""
-    tmp = _LIB + ".tmp"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"], check=True)
+    """Compile the oracle's C files into _liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp] + _SRCS + ["-lm"], check=True)
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -39,13 +40,17 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SRCS):
             build()
         lib = ctypes.CDLL(_LIB)
         lib.oracle_dsa_lane.restype = ctypes.c_int
         lib.oracle_dsa_lane.argtypes = [ctypes.c_int] * 6 + [_P] * 13
         lib.oracle_dense_lane.restype = ctypes.c_int
         lib.oracle_dense_lane.argtypes = [ctypes.c_int] * 3 + [_P] * 6
+        lib.oracle_window_lane.restype = ctypes.c_int
+        lib.oracle_window_lane.argtypes = [ctypes.c_int] * 5 + [_P] * 8
+        lib.oracle_score_lane.restype = ctypes.c_int
+        lib.oracle_score_lane.argtypes = [ctypes.c_int] * 6 + [_P] * 12
         _lib = lib
     return _lib
 
@@ -120,6 +125,66 @@ def run_dense_lane(L_p, q, kp, vp, k, v):
     if rc != 0:
         raise ValueError("oracle_dense_lane failed (%d)" % rc)
     return out
+
+
+def run_window_lane(L_p, N_att, sink, q, kp, vp, k, v, masks=False):
+    """SlidingWindow (sink 0) or StreamingLLM (sink 4) on one lane for T = len(q) steps.
+
+    Returns out [T][d], n_dec [T] and, on request, att_mask [T][T].
+    """
+    T, d = np.shape(q)
+    q, k, v = _f64(q, (T, d)), _f64(k, (T, d)), _f64(v, (T, d))
+    kp, vp = _f64(kp, (L_p, d)), _f64(vp, (L_p, d))
+    out = np.empty((T, d), np.float64)
+    n_dec = np.empty(T, np.int32)
+    att = np.zeros((T, T), np.uint8) if masks else None
+    rc = _load().oracle_window_lane(L_p, N_att, sink, d, T, _ptr(q), _ptr(kp), _ptr(vp), _ptr(k), _ptr(v),
+                                    _ptr(out), _ptr(n_dec), _ptr(att))
+    if rc != 0:
+        raise ValueError("oracle_window_lane failed (%d)" % rc)
+    res = {"out": out, "n_dec": n_dec}
+    if masks:
+        res["att_mask"] = att.astype(bool)
+    return res
+
+
+TOVA, H2O = 0, 1
+
+
+def run_score_lane(policy, L_p, N_att, q, kp, vp, k, v, N_recent=0, follow=None, masks=False, scores=False):
+    """TOVA (policy 0) or H2O (policy 1, N_recent protected recent positions) on one lane.
+
+    follow: optional int array [T]: at eviction steps the entry that leaves is
+    follow[t] instead of the oracle's own choice (it must be a candidate).
+    Returns out [T][d], choice [T] (position the step's own rule evicts, -1 if
+    none), n_dec [T], gap [T] (with follow) and, on request, att_mask [T][T]
+    and score [T][T] (H2O accumulated scores after each step).
+    """
+    T, d = np.shape(q)
+    q, k, v = _f64(q, (T, d)), _f64(k, (T, d)), _f64(v, (T, d))
+    kp, vp = _f64(kp, (L_p, d)), _f64(vp, (L_p, d))
+    out = np.empty((T, d), np.float64)
+    choice = np.empty(T, np.int32)
+    n_dec = np.empty(T, np.int32)
+    fol = None if follow is None else np.ascontiguousarray(follow, dtype=np.int32)
+    gap = np.zeros(T, np.float64) if follow is not None else None
+    att = np.zeros((T, T), np.uint8) if masks else None
+    sc = np.zeros((T, T), np.float64) if scores else None
+    rc = _load().oracle_score_lane(policy, L_p, N_att, N_recent, d, T, _ptr(q), _ptr(kp), _ptr(vp), _ptr(k),
+                                   _ptr(v), _ptr(fol), _ptr(out), _ptr(choice), _ptr(n_dec), _ptr(gap), _ptr(att),
+                                   _ptr(sc))
+    if rc == -2:
+        raise ValueError("follow names a position that is not a candidate")
+    if rc != 0:
+        raise ValueError("oracle_score_lane failed (%d)" % rc)
+    res = {"out": out, "choice": choice, "n_dec": n_dec}
+    if gap is not None:
+        res["gap"] = gap
+    if masks:
+        res["att_mask"] = att.astype(bool)
+    if scores:
+        res["score"] = sc
+    return res
 
 
 def lane_inputs(workload, layer, b, h, T=None):
