@@ -16,6 +16,8 @@ import numpy as np
 from . import _build
 
 DSA_F32, DSA_BF16 = 0, 1
+(DSA_POLICY_DIAGONAL, DSA_POLICY_DIAGONAL_SINK4, DSA_POLICY_SLIDING_WINDOW, DSA_POLICY_STREAMING_LLM, DSA_POLICY_TOVA,
+ DSA_POLICY_H2O) = range(6)
 
 _c_int, _c_size, _P = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -23,6 +25,8 @@ _c_int, _c_size, _P = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIGNATURES = {
     "dsa_state_workspace_bytes": (_c_size, [_c_int] * 8),
     "dsa_state_init": (_c_int, [ctypes.POINTER(_P)] + [_c_int] * 8 + [_P, _c_size, _P]),
+    "dsa_policy_workspace_bytes": (_c_size, [_c_int] * 8),
+    "dsa_policy_state_init": (_c_int, [ctypes.POINTER(_P)] + [_c_int] * 8 + [_P, _c_size, _P]),
     "dsa_set_stream": (_c_int, [_P, _P]),
     "dsa_append_prompt": (_c_int, [_P, _P, _P]),
     "dsa_append_kv": (_c_int, [_P, _P, _P]),
@@ -137,6 +141,19 @@ def dsa_state_init(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype, workspa
     return State(h, "sparse", batch * heads, N_att - sink, workspace)
 
 
+def dsa_policy_workspace_bytes(policy, batch, L_p, N_r, N_att, heads, head_dim, dtype) -> int:
+    return int(library().dsa_policy_workspace_bytes(policy, batch, L_p, N_r, N_att, heads, head_dim, dtype))
+
+
+def dsa_policy_state_init(policy, batch, L_p, N_r, N_att, heads, head_dim, dtype, workspace, workspace_bytes,
+                          stream=None):
+    h = _P()
+    _check(library().dsa_policy_state_init(ctypes.byref(h), policy, batch, L_p, N_r, N_att, heads, head_dim, dtype,
+                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+    sink = 4 if policy in (DSA_POLICY_DIAGONAL_SINK4, DSA_POLICY_STREAMING_LLM) else 0
+    return State(h, "sparse", batch * heads, N_att - sink, workspace)
+
+
 def dsa_set_stream(st, stream):
     return _check(library().dsa_set_stream(st, _stream(stream)))
 
@@ -154,7 +171,9 @@ def dsa_decode_step(st, q_t, out, trace=None):
 
 
 def dsa_read_state(st):
-    """Returns (t, offsets [lanes][N_att - sink] int16 padded with -1, counts [lanes] int32)."""
+    """Returns (t, offsets [lanes][N_att - sink] int16 padded with -1, counts [lanes] int32).
+
+    TOVA / H2O states list N_att offsets (sink 0)."""
     t = ctypes.c_int32()
     offs = np.empty((st.lanes, st.list_len), np.int16)
     cnt = np.empty(st.lanes, np.int32)

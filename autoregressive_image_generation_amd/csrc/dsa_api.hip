@@ -34,12 +34,15 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Kind { KIND_SPARSE = 1, KIND_DENSE = 2 };
+// SPARSE: Algorithm 1 and its equal-budget cases (SlidingWindow,
+// StreamingLLM); DENSE: no sparsity; SCORE: TOVA and H2O over N_att slots.
+enum Kind { KIND_SPARSE = 1, KIND_DENSE = 2, KIND_SCORE = 3 };
 
 }  // namespace
 
 struct dsa_state {
     int kind;
+    int policy;  // dsa_policy
     int batch, heads, D, L_p, N_r, N_att, S, dtype, L_max;
     int lanes, N_rw, N_attw, list_stride;
     long long lane_rows;
@@ -52,6 +55,9 @@ struct dsa_state {
     const void* pend_k;
     const void* pend_v;
     int waves;
+    // SCORE states: per-lane slot metadata and (H2O) accumulated scores
+    size_t meta_off, score_off;
+    int meta_stride, score_stride, n_recent;
 };
 
 namespace {
@@ -98,12 +104,21 @@ int check_workspace(void* ws, size_t have, size_t need) {
     return 0;
 }
 
-int check_state(const dsa_state* st, int kind) {
+const char* kind_name(int kind) {
+    return kind == KIND_SPARSE ? "sparse" : kind == KIND_DENSE ? "dense" : "score-policy";
+}
+
+int check_state(const dsa_state* st, int kind, int kind2 = -1) {
     if (!st) return fail(DSA_E_INVAL, "state is NULL");
-    if (kind && st->kind != kind)
-        return fail(DSA_E_INVAL, "state is a %s state", st->kind == KIND_SPARSE ? "sparse" : "dense");
+    if (kind && st->kind != kind && st->kind != kind2) return fail(DSA_E_INVAL, "state is a %s state", kind_name(st->kind));
     return 0;
 }
+
+// Score-policy (TOVA / H2O) sizes: [0] free slot, [4 + j] slot positions, in
+// 16-byte chunks; the H2O logits of one lane live in LDS next to them.
+int meta_stride_for(int N_att) { return (4 + N_att + 3) / 4 * 4; }
+int score_stride_for(int N_att) { return (N_att + 1) / 2 * 2; }
+constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 
 // Wavefronts per workgroup.  Measured on MI355X: the decode is fastest with
 // one to three thousand wavefronts per launch in total (one workgroup per
@@ -124,7 +139,7 @@ int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
         if (!k_p || !v_p) return fail(DSA_E_INVAL, "prompt pointers are NULL");
         if (!aligned16(k_p) || !aligned16(v_p)) return fail(DSA_E_INVAL, "prompt pointers must be 16-byte aligned");
     }
-    const bool init_list = st->kind == KIND_SPARSE && st->S == 0;
+    const bool init_list = st->kind == KIND_SPARSE && st->S == 0;  // score states need no initial data
     if (st->L_p > 0 || init_list) {
         dsa::PromptArgs a;
         a.k_p = k_p;
@@ -178,6 +193,107 @@ void fill_common(const dsa_state* st, const void* q_t, float* out, dsa::DecodeAr
     a.scale_log2e = 1.4426950408889634 / sqrt((double)st->D);
 }
 
+// Map a dsa_policy onto a state kind.  Diagonal (with or without sinks)
+// takes N_r as given; SlidingWindow and StreamingLLM are Algorithm 1 with the
+// ring as long as the attended budget (no selection ever happens), so N_r must
+// equal N_att; TOVA keeps N_att slots and N_r must equal N_att too; H2O keeps
+// N_att slots of which the N_r most recent positions are protected.
+int resolve_policy(int policy, int N_r, int N_att, int* kind, int* sink) {
+    switch (policy) {
+        case DSA_POLICY_DIAGONAL: *kind = KIND_SPARSE; *sink = 0; return 0;
+        case DSA_POLICY_DIAGONAL_SINK4: *kind = KIND_SPARSE; *sink = 4; return 0;
+        case DSA_POLICY_SLIDING_WINDOW:
+        case DSA_POLICY_STREAMING_LLM:
+        case DSA_POLICY_TOVA:
+            if (N_r != N_att) return fail(DSA_E_INVAL, "this policy keeps N_att entries: N_r (%d) must equal N_att (%d)", N_r, N_att);
+            *kind = policy == DSA_POLICY_TOVA ? KIND_SCORE : KIND_SPARSE;
+            *sink = policy == DSA_POLICY_STREAMING_LLM ? 4 : 0;
+            return 0;
+        case DSA_POLICY_H2O:
+            if (N_r < 1 || N_r >= N_att)
+                return fail(DSA_E_INVAL, "H2O: the protected recent count N_r (%d) must be in [1, N_att - 1] (N_att = %d)", N_r, N_att);
+            *kind = KIND_SCORE;
+            *sink = 0;
+            return 0;
+        default: return fail(DSA_E_INVAL, "unknown policy %d", policy);
+    }
+}
+
+int check_score(int policy, int batch, int L_p, int N_att, int heads, int head_dim, int dtype) {
+    int rc = check_common(batch, L_p, heads, head_dim, dtype);
+    if (rc) return rc;
+    if (N_att < 1 || N_att > DSA_MAX_ATTEND) return fail(DSA_E_INVAL, "N_att must be in [1, %d] (got %d)", DSA_MAX_ATTEND, N_att);
+    if (policy == DSA_POLICY_H2O && (long long)L_p + N_att > kMaxH2oRows)
+        return fail(DSA_E_INVAL, "H2O needs L_p + N_att <= %d (got %lld)", kMaxH2oRows, (long long)L_p + N_att);
+    return 0;
+}
+
+size_t score_workspace_bytes(int policy, int batch, int L_p, int N_att, int heads, int head_dim, int dtype) {
+    const long long lanes = (long long)batch * heads;
+    size_t b = kv_bytes(lanes, (long long)L_p + N_att, head_dim, dtype) +
+               align_up((size_t)lanes * (size_t)meta_stride_for(N_att) * sizeof(int32_t));
+    if (policy == DSA_POLICY_H2O) b += align_up((size_t)lanes * (size_t)score_stride_for(N_att) * sizeof(double));
+    return b;
+}
+
+int score_decode(dsa_state* st, const void* q_t, float* out, int32_t* trace) {
+    dsa::DecodeArgs a;
+    fill_common(st, q_t, out, a);
+    const int t = st->t, N = st->N_att;
+    a.trace = trace;
+    a.meta = reinterpret_cast<int32_t*>(st->ws + st->meta_off);
+    a.score = st->policy == DSA_POLICY_H2O ? reinterpret_cast<double*>(st->ws + st->score_off) : nullptr;
+    a.meta_stride = st->meta_stride;
+    a.score_stride = st->score_stride;
+    a.N_cache = N;
+    a.n_occ = std::min(t, N - 1);
+    a.n_meta = 4 + std::min(t, N);
+    a.free_host = t < N ? t : -1;  // while the cache fills, token t takes slot t
+    a.select = t >= N - 1 ? 1 : 0;  // the cache is full once token t is in it
+    a.n_recent = st->n_recent;
+    a.inv_sqrt_d = 1.0 / sqrt((double)st->D);
+    a.evicted = -1;
+    const int waves = choose_waves(st, (long long)st->L_p + std::min(t + 1, N));
+    const int mode = st->policy == DSA_POLICY_H2O ? dsa::MODE_H2O : dsa::MODE_TOVA;
+    hipError_t e = dsa::launch_decode(mode, st->dtype, st->D, waves, a, st->stream);
+    if (e != hipSuccess) return hip_fail(e, "score-policy decode launch");
+    st->pend_k = st->pend_v = nullptr;
+    st->t += 1;
+    return DSA_OK;
+}
+
+// Attended-entry offsets of the next step of a score state, read from the slot metadata.
+int score_read_state(const dsa_state* st, int16_t* h_offsets, int32_t* h_count) {
+    const int tn = st->t, N = st->N_att;
+    std::vector<int32_t> buf;
+    try {
+        buf.resize((size_t)st->lanes * st->meta_stride);
+    } catch (...) {
+        return fail(DSA_E_NOMEM, "host allocation failed");
+    }
+    hipError_t e = hipStreamSynchronize(st->stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    e = hipMemcpy(buf.data(), st->ws + st->meta_off, buf.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "slot metadata copy");
+    const int occ = std::min(tn, N);  // slots holding a position before step tn
+    std::vector<int> offs;
+    for (int l = 0; l < st->lanes; ++l) {
+        const int32_t* m = buf.data() + (size_t)l * st->meta_stride;
+        const int free_slot = tn < N ? tn : m[0];
+        offs.clear();
+        offs.push_back(0);  // the next token itself
+        for (int j = 0; j < occ; ++j)
+            if (j != free_slot) offs.push_back(tn - m[4 + j]);
+        std::sort(offs.begin(), offs.end());
+        if (h_offsets) {
+            int16_t* dst = h_offsets + (size_t)l * N;
+            for (int j = 0; j < N; ++j) dst[j] = j < (int)offs.size() ? (int16_t)std::min(offs[j], 32767) : (int16_t)-1;
+        }
+        if (h_count) h_count[l] = (int)offs.size();
+    }
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +317,7 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     dsa_state* st = new (std::nothrow) dsa_state();
     if (!st) return fail(DSA_E_NOMEM, "host allocation failed");
     st->kind = KIND_SPARSE;
+    st->policy = sink ? DSA_POLICY_DIAGONAL_SINK4 : DSA_POLICY_DIAGONAL;
     st->batch = batch;
     st->heads = heads;
     st->D = head_dim;
@@ -223,6 +340,57 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     return DSA_OK;
 }
 
+size_t dsa_policy_workspace_bytes(int policy, int batch, int L_p, int N_r, int N_att, int heads, int head_dim,
+                                  int dtype) {
+    int kind, sink;
+    if (resolve_policy(policy, N_r, N_att, &kind, &sink)) return 0;
+    if (kind == KIND_SPARSE) return dsa_state_workspace_bytes(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype);
+    if (check_score(policy, batch, L_p, N_att, heads, head_dim, dtype)) return 0;
+    return score_workspace_bytes(policy, batch, L_p, N_att, heads, head_dim, dtype);
+}
+
+int dsa_policy_state_init(dsa_state** out, int policy, int batch, int L_p, int N_r, int N_att, int heads,
+                          int head_dim, int dtype, void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!out) return fail(DSA_E_INVAL, "out handle pointer is NULL");
+    int kind, sink;
+    int rc = resolve_policy(policy, N_r, N_att, &kind, &sink);
+    if (rc) return rc;
+    if (kind == KIND_SPARSE) {
+        rc = dsa_state_init(out, batch, L_p, N_r, N_att, heads, head_dim, sink, dtype, d_workspace, workspace_bytes,
+                            hip_stream);
+        if (rc == DSA_OK) (*out)->policy = policy;
+        return rc;
+    }
+    rc = check_score(policy, batch, L_p, N_att, heads, head_dim, dtype);
+    if (rc) return rc;
+    rc = check_workspace(d_workspace, workspace_bytes,
+                         score_workspace_bytes(policy, batch, L_p, N_att, heads, head_dim, dtype));
+    if (rc) return rc;
+    dsa_state* st = new (std::nothrow) dsa_state();
+    if (!st) return fail(DSA_E_NOMEM, "host allocation failed");
+    st->kind = KIND_SCORE;
+    st->policy = policy;
+    st->batch = batch;
+    st->heads = heads;
+    st->D = head_dim;
+    st->L_p = L_p;
+    st->N_r = N_r;
+    st->N_att = N_att;
+    st->dtype = dtype;
+    st->lanes = batch * heads;
+    st->lane_rows = (long long)L_p + N_att;
+    st->ws = static_cast<char*>(d_workspace);
+    st->ws_bytes = workspace_bytes;
+    st->meta_stride = meta_stride_for(N_att);
+    st->score_stride = score_stride_for(N_att);
+    st->meta_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    st->score_off = st->meta_off + align_up((size_t)st->lanes * (size_t)st->meta_stride * sizeof(int32_t));
+    st->n_recent = policy == DSA_POLICY_H2O ? N_r : 0;
+    st->stream = static_cast<hipStream_t>(hip_stream);
+    *out = st;
+    return DSA_OK;
+}
+
 int dsa_set_stream(dsa_state* st, void* hip_stream) {
     int rc = check_state(st, 0);
     if (rc) return rc;
@@ -231,21 +399,22 @@ int dsa_set_stream(dsa_state* st, void* hip_stream) {
 }
 
 int dsa_append_prompt(dsa_state* st, const void* k_p, const void* v_p) {
-    int rc = check_state(st, KIND_SPARSE);
+    int rc = check_state(st, KIND_SPARSE, KIND_SCORE);
     return rc ? rc : launch_prompt(st, k_p, v_p);
 }
 
 int dsa_append_kv(dsa_state* st, const void* k_t, const void* v_t) {
-    int rc = check_state(st, KIND_SPARSE);
+    int rc = check_state(st, KIND_SPARSE, KIND_SCORE);
     return rc ? rc : record_kv(st, k_t, v_t);
 }
 
 int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) {
-    int rc = check_state(st, KIND_SPARSE);
+    int rc = check_state(st, KIND_SPARSE, KIND_SCORE);
     if (rc) return rc;
     rc = check_step(st, q_t, out);
     if (rc) return rc;
     if (trace && ((uintptr_t)trace & 7u)) return fail(DSA_E_INVAL, "trace must be 8-byte aligned");
+    if (st->kind == KIND_SCORE) return score_decode(st, q_t, out, trace);
 
     dsa::DecodeArgs a;
     fill_common(st, q_t, out, a);
@@ -278,8 +447,18 @@ int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) 
 }
 
 int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_t* h_count) {
-    int rc = check_state(st, KIND_SPARSE);
+    int rc = check_state(st, KIND_SPARSE, KIND_SCORE);
     if (rc) return rc;
+    if (st->kind == KIND_SCORE) {
+        rc = (h_offsets || h_count) ? score_read_state(st, h_offsets, h_count) : 0;
+        if (rc) return rc;
+        if (!h_offsets && !h_count) {
+            hipError_t e = hipStreamSynchronize(st->stream);
+            if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+        }
+        if (h_t) *h_t = st->t;
+        return DSA_OK;
+    }
     const int tw = st->t - st->S;
     const int n = tw < 0 ? 0 : std::min(tw + 1, st->N_attw);
     if (h_offsets || h_count) {

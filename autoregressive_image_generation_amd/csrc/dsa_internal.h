@@ -7,7 +7,10 @@
 
 namespace dsa {
 
-enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1 };
+// SPARSE: Algorithm 1 (also SlidingWindow / StreamingLLM as its equal-budget
+// cases); DENSE: no sparsity; TOVA, H2O: the score-based baselines over a
+// cache of N_att slots per lane.
+enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_TOVA = 2, MODE_H2O = 3 };
 
 // Everything one decode launch needs.  Host-computed per step: all lanes of a
 // state share t, so the phase logic of Algorithm 1 (page 4, Section 4) is
@@ -36,6 +39,17 @@ struct DecodeArgs {
     int self_row;          // cache row (after the prompt rows) the appended K/V goes to
     int evicted;           // sparse: position evicted at this step, or -1
     double scale_log2e;    // log2(e) / sqrt(D)
+    // TOVA / H2O (slot cache; cache rows L_p .. L_p + N_cache - 1 are the slots)
+    int32_t* meta;         // [lanes][meta_stride]: [0] free slot, [4 + j] position held by slot j
+    double* score;         // H2O: [lanes][score_stride] accumulated score of slot j
+    int meta_stride;       // 4 + N_cache rounded up to 4 (16 bytes)
+    int score_stride;      // N_cache rounded up to 2
+    int N_cache;           // slots per lane (N_att)
+    int n_occ;             // occupied slots attended besides the current token: min(t, N_cache - 1)
+    int n_meta;            // meta entries this step reads: 4 + min(t, N_cache)
+    int free_host;         // slot of the current token when the host knows it (t < N_cache), else -1
+    int n_recent;          // H2O: protected most recent positions
+    double inv_sqrt_d;     // H2O: 1 / sqrt(D), for the fp64 probabilities
 };
 
 struct PromptArgs {

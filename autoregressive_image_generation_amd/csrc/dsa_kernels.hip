@@ -1,8 +1,10 @@
 // Decode-attention kernels for gfx950 (CDNA4): the fused diagonal-aware sparse
 // step of "Understanding and Exploiting Diagonal Attention Sparsity in
 // Autoregressive Image Generation" (Section 4, Algorithm 1; Section 5.1 for the
-// fused gather + argmin design and the Diagonal+Sink4 variant) and the dense
-// decode step it is compared with.
+// fused gather + argmin design and the Diagonal+Sink4 variant), the dense
+// decode step it is compared with, and the score-based baselines of Sections
+// 2.3 and 5.1: TOVA (the lowest-scoring entry of the step leaves the cache)
+// and H2O (the unprotected entry with the lowest accumulated score leaves).
 //
 // One workgroup per lane (one (sequence, head) of the layer), `waves` 64-wide
 // wavefronts.  A row of the cache is K (D elements) followed by V (D
@@ -116,17 +118,37 @@ __device__ __forceinline__ bool better(double s, int d, double bs, int bd) {
     return s < bs || (s == bs && d > bd);
 }
 
-// EARLY: every thread group's first U rows need no list entry (U * G <= number
-// of prompt + sink rows), so they are requested before the list has arrived.
+// Wavefront-wide reductions of doubles (butterfly: every lane ends with the result).
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// EARLY: every thread group's first U rows need no list or slot entry (U * G
+// <= number of prompt + sink rows), so they are requested before the lane's
+// index data has arrived.
 template <typename T, int D, int MODE, int U, bool EARLY>
 __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     constexpr int EPT = Traits<T>::EPT;
     constexpr int TPR = D / EPT;          // threads per half-row
     constexpr int GPW = 64 / TPR;         // thread groups per wavefront
     constexpr int ROW = 2 * D;            // elements per cache row
+    constexpr bool SLOTS = MODE == MODE_TOVA || MODE == MODE_H2O;
 
-    extern __shared__ uint4 s_list16[];   // sparse: the lane's attended offsets
-    int16_t* s_list = reinterpret_cast<int16_t*>(s_list16);
+    // Dynamic LDS: the lane's index data, staged once per launch.  Sparse: the
+    // attended window offsets (int16).  TOVA / H2O: the slot metadata (int32:
+    // [0] the free slot, [4 + j] the position slot j holds), then for H2O the
+    // fp64 logit of every attended row.
+    extern __shared__ uint4 s_dyn16[];
+    int16_t* s_list = reinterpret_cast<int16_t*>(s_dyn16);
+    const int32_t* s_meta = reinterpret_cast<const int32_t*>(s_dyn16);
+    double* s_logit = reinterpret_cast<double*>(s_dyn16 + a.meta_stride / 4);
     __shared__ float s_m[kMaxWaves], s_l[kMaxWaves];
     __shared__ float s_acc[kMaxWaves][D];
     __shared__ double s_bs[kMaxWaves];
@@ -145,47 +167,70 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     const T* k_self = reinterpret_cast<const T*>(a.k_new) + (size_t)lane * D;
     const T* v_self = reinterpret_cast<const T*>(a.v_new) + (size_t)lane * D;
 
-    const int R = MODE == MODE_SPARSE ? a.L_p + a.n_sink + a.n_list : a.L_p + a.t + 1;
-    const int win0 = MODE == MODE_SPARSE ? a.L_p + a.n_sink : R;  // first listed row
+    // Rows [0, R): prompt rows, then sinks (sparse) or cached decode positions
+    // (dense), then from win0 on the listed window entries (sparse) or the
+    // occupied slots and the current token (TOVA / H2O).
+    const int R = MODE == MODE_SPARSE ? a.L_p + a.n_sink + a.n_list
+                  : MODE == MODE_DENSE ? a.L_p + a.t + 1
+                                       : a.L_p + a.n_occ + 1;
+    const int win0 = MODE == MODE_SPARSE ? a.L_p + a.n_sink : MODE == MODE_DENSE ? R : a.L_p;
     constexpr int CH = ROW * (int)sizeof(T) / 16;                // 16-byte chunks per row
 
-    // Requests in the order their data is needed: the index list (16 bytes =
-    // 8 offsets per load; the list stride is padded to whole chunks), the
-    // query chunk, the appended row, then (EARLY) the first prompt rows.
-    // Vector loads complete in issue order, so waiting for the list only
-    // waits for what was issued before it.
-    const int nch = (a.n_list + 7) / 8;
-    const uint4* lst16 = reinterpret_cast<const uint4*>(a.list + (size_t)lane * a.list_stride);
+    // Requests in the order their data is needed: the index data (16-byte
+    // chunks; strides are padded to whole chunks), the query chunk, the
+    // appended row, then (EARLY) the first prompt rows.  Vector loads complete
+    // in issue order, so waiting for the index data only waits for what was
+    // issued before it.
+    const int nch = MODE == MODE_SPARSE ? (a.n_list + 7) / 8 : SLOTS ? (a.n_meta + 3) / 4 : 0;
+    const uint4* idx16 = MODE == MODE_SPARSE ? reinterpret_cast<const uint4*>(a.list + (size_t)lane * a.list_stride)
+                                             : reinterpret_cast<const uint4*>(a.meta + (size_t)lane * a.meta_stride);
     uint4 lc0 = make_uint4(0, 0, 0, 0), lc1 = make_uint4(0, 0, 0, 0);
-    if constexpr (MODE == MODE_SPARSE) {
-        if (tid < nch) lc0 = load16(lst16 + tid);
-        if (tid + (int)blockDim.x < nch) lc1 = load16(lst16 + tid + blockDim.x);
+    if constexpr (MODE != MODE_DENSE) {
+        if (tid < nch) lc0 = load16(idx16 + tid);
+        if (tid + (int)blockDim.x < nch) lc1 = load16(idx16 + tid + blockDim.x);
     }
     const uint4 qx = load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT);
     uint4 ax = make_uint4(0, 0, 0, 0);
     if (tid < CH) ax = load16((tid < CH / 2 ? k_self : v_self) + (tid % (CH / 2)) * EPT);
 
-    // Source of row r in [0, R): prompt rows, then sinks (sparse) or cached
-    // decode positions (dense) in their own cache rows, then the listed window
-    // entries: offset d = t - position, ring slot S + (t' - d) mod N_rw.  The
-    // current token is read from k_new / v_new.  Branch-free, so that the row
-    // loads below are straight-line code and every wait on them is exact.
+    // TOVA / H2O: the slot the current token takes (the one freed by the last
+    // eviction, or the next empty one while the cache fills).
+    int fslot = SLOTS && a.free_host >= 0 ? a.free_host : 0;
+
+    // Source of row r in [0, R).  Sparse: offset d = t - position of the
+    // listed entry, ring slot S + (t' - d) mod N_rw.  TOVA / H2O: the j-th
+    // occupied slot skips the free one; the last row is the current token.
+    // The current token is read from k_new / v_new.  Branch-free, so that the
+    // row loads below are straight-line code and every wait on them is exact.
     auto row_src = [&](int r, const T*& kr, const T*& vr, int& d) {
         const bool listed = r >= win0;
-        int dl = 0;
+        bool self;
+        int row;
+        d = -1;
         if constexpr (MODE == MODE_SPARSE) {
             // Offsets are written only by this kernel and lie in [0, N_rw);
             // the clamp keeps a damaged workspace from turning into stray reads.
-            dl = min(max((int)s_list[max(r - win0, 0)], 0), a.N_rw - 1);
+            const int dl = min(max((int)s_list[max(r - win0, 0)], 0), a.N_rw - 1);
+            int slot = a.base - dl;
+            slot += slot < 0 ? a.N_rw : 0;
+            // the current token is a listed entry (offset 0) or, while t < S, a sink
+            self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
+            row = listed ? a.L_p + a.S + slot : r;
+            d = listed ? dl : -1;
+        } else if constexpr (MODE == MODE_DENSE) {
+            self = r >= a.L_p && r - a.L_p == a.t;
+            row = r;
+        } else {
+            const int j = max(r - win0, 0);
+            const bool me = j == a.n_occ;
+            const int slot = min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
+            self = listed && me;
+            row = listed ? a.L_p + slot : r;
+            d = listed ? (me ? 0 : a.t - s_meta[4 + slot]) : -1;
         }
-        int slot = a.base - dl;
-        slot += slot < 0 ? a.N_rw : 0;
-        const bool self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
-        const int row = listed ? a.L_p + a.S + slot : r;
         const T* base = lane_kv + (size_t)row * ROW;
         kr = self ? k_self : base;
         vr = self ? v_self : base + D;
-        d = listed ? dl : -1;
     };
 
     // Rows of this group: r_k = g + k * G.  Every group of a wavefront runs the
@@ -206,12 +251,16 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
             vx[u] = load16_stream(vr + sl * EPT);
         }
     };
-    if constexpr (EARLY) first_rows();  // prompt rows only: no list entry read
-    if constexpr (MODE == MODE_SPARSE) {
-        if (tid < nch) s_list16[tid] = lc0;
-        if (tid + (int)blockDim.x < nch) s_list16[tid + blockDim.x] = lc1;
-        for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_list16[c] = load16(lst16 + c);
+    if constexpr (EARLY) first_rows();  // prompt rows only: no index data read
+    if constexpr (MODE != MODE_DENSE) {
+        if (tid < nch) s_dyn16[tid] = lc0;
+        if (tid + (int)blockDim.x < nch) s_dyn16[tid + blockDim.x] = lc1;
+        for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_dyn16[c] = load16(idx16 + c);
         __syncthreads();
+    }
+    if constexpr (SLOTS) {
+        // free slot: clamped like the offsets above
+        if (a.free_host < 0) fslot = min(max(s_meta[0], 0), a.N_cache - 1);
     }
     if constexpr (!EARLY) first_rows();
 
@@ -235,6 +284,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     // selects instead of branches, so the loop below stays straight-line.
     auto consume = [&](int k, const uint4& kq, const uint4& vq, int d) {
         const bool valid = k < nk;
+        const int r = g + k * G;
         float kf[EPT], vf[EPT];
         unpack<T>(kq, kf);
         unpack<T>(vq, vf);
@@ -242,11 +292,16 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
         const double s = group_sum<TPR>(part);
-        if constexpr (MODE == MODE_SPARSE) {
+        if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
             const bool cand = valid && a.select && d >= 0 && better(s, d, best_s, best_d);
+            int jj = r - win0;  // sparse: list index
+            if constexpr (MODE == MODE_TOVA) jj = jj == a.n_occ ? fslot : jj + (jj >= fslot ? 1 : 0);  // slot
             best_s = cand ? s : best_s;
             best_d = cand ? d : best_d;
-            best_j = cand ? g + k * G - win0 : best_j;
+            best_j = cand ? jj : best_j;
+        }
+        if constexpr (MODE == MODE_H2O) {
+            if (valid && sl == 0) s_logit[r] = s;
         }
         const float x = valid ? (float)(s * a.scale_log2e) : -__builtin_inff();
         const float mn = fmaxf(sm.m, x);
@@ -276,11 +331,12 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) consume(k0 + u, kx[u], vx[u], dd[u]);
 
     // Append: the new K/V row goes to its cache row.  Nothing this launch
-    // reads lives there (it is empty, or holds the entry evicted at this step);
-    // the current token itself is read from k_new / v_new.  Loaded at the
-    // start, stored here, so it adds no latency of its own.
+    // reads lives there (it is empty, holds the entry evicted at this step, or
+    // is the free slot); the current token itself is read from k_new / v_new.
+    // Loaded at the start, stored here, so it adds no latency of its own.
     if (tid < CH) {
-        T* dst = const_cast<T*>(lane_kv) + (size_t)(a.L_p + a.self_row) * ROW + (tid / (CH / 2)) * D +
+        const int self_row = SLOTS ? fslot : a.self_row;
+        T* dst = const_cast<T*>(lane_kv) + (size_t)(a.L_p + self_row) * ROW + (tid / (CH / 2)) * D +
                  (tid % (CH / 2)) * EPT;
         *reinterpret_cast<uint4*>(dst) = ax;
     }
@@ -294,7 +350,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) acc2[e] = __shfl_xor(acc[e], o);
         merge<EPT>(sm, acc, m2, l2, acc2);
-        if constexpr (MODE == MODE_SPARSE) {
+        if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
             const double bs2 = __shfl_xor(best_s, o);
             const int bd2 = __shfl_xor(best_d, o);
             const int bj2 = __shfl_xor(best_j, o);
@@ -319,21 +375,23 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    if (wave != 0 || wl >= TPR) return;
+    if (wave != 0) return;
 
-    for (int w = 1; w < nwaves; ++w) {
-        float acc2[EPT];
+    if (wl < TPR) {
+        for (int w = 1; w < nwaves; ++w) {
+            float acc2[EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc2[e] = s_acc[w][sl * EPT + e];
-        merge<EPT>(sm, acc, s_m[w], s_l[w], acc2);
+            for (int e = 0; e < EPT; ++e) acc2[e] = s_acc[w][sl * EPT + e];
+            merge<EPT>(sm, acc, s_m[w], s_l[w], acc2);
+        }
+        const float inv = 1.0f / sm.l;
+        float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4)
+            o4[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
     }
-    const float inv = 1.0f / sm.l;
-    float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
-#pragma unroll
-    for (int e = 0; e < EPT; e += 4)
-        o4[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
 
-    if constexpr (MODE == MODE_SPARSE) {
+    if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
         if (wl != 0) return;
         for (int w = 1; w < nwaves; ++w) {
             if (s_bd[w] >= 0 && (best_d < 0 || better(s_bs[w], s_bd[w], best_s, best_d))) {
@@ -342,21 +400,88 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
                 best_j = s_bj[w];
             }
         }
-        int16_t* lst = a.list + (size_t)lane * a.list_stride;
         int chosen = -1;
-        if (a.select) {
-            // skip_idx.append(idx[j*]): offset best_d leaves the attended list
-            // for good; the offset entering the window at t+1 takes its place.
-            if (best_j >= 0) {
-                chosen = a.t - best_d;
-                lst[best_j] = (int16_t)a.add_off;
+        if constexpr (MODE == MODE_SPARSE) {
+            int16_t* lst = a.list + (size_t)lane * a.list_stride;
+            if (a.select) {
+                // skip_idx.append(idx[j*]): offset best_d leaves the attended list
+                // for good; the offset entering the window at t+1 takes its place.
+                if (best_j >= 0) {
+                    chosen = a.t - best_d;
+                    lst[best_j] = (int16_t)a.add_off;
+                }
+            } else if (a.add_off >= 0 && a.n_list < a.N_attw) {
+                lst[a.n_list] = (int16_t)a.add_off;
             }
-        } else if (a.add_off >= 0 && a.n_list < a.N_attw) {
-            lst[a.n_list] = (int16_t)a.add_off;
+        } else {
+            // TOVA: the current token holds its slot; with a full cache the
+            // lowest-logit entry leaves and its slot is the next free one.
+            int32_t* meta = a.meta + (size_t)lane * a.meta_stride;
+            meta[4 + fslot] = a.t;
+            if (a.select && best_j >= 0) {
+                chosen = a.t - best_d;
+                meta[0] = best_j;
+            }
         }
         if (a.trace) {
             a.trace[2 * lane] = chosen;
-            a.trace[2 * lane + 1] = a.evicted;
+            a.trace[2 * lane + 1] = MODE == MODE_SPARSE ? a.evicted : -1;
+        }
+    }
+
+    if constexpr (MODE == MODE_H2O) {
+        // Accumulated scores in fp64: each attended decode entry adds its
+        // probability under this step's softmax (prompt rows included in the
+        // normalisation); then, with a full cache, the unprotected entry
+        // (position <= t - n_recent) with the lowest score leaves, the lowest
+        // position among equals.  Wave 0 does this for the lane.
+        const double c = a.inv_sqrt_d;
+        double m = -__builtin_inf();
+        for (int r = wl; r < R; r += 64) m = fmax(m, s_logit[r]);
+        m = wave_max(m);
+        double l = 0.0;
+        for (int r = wl; r < R; r += 64) l += exp((s_logit[r] - m) * c);
+        l = wave_sum(l);
+        double* sc = a.score + (size_t)lane * a.score_stride;
+        const int lim = a.t - a.n_recent;
+        double bkey = __builtin_inf();
+        int bpos = 0x7fffffff, bslot = -1;
+        for (int j = wl; j <= a.n_occ; j += 64) {
+            const bool me = j == a.n_occ;
+            const int slot = me ? fslot : min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
+            const double p = exp((s_logit[win0 + j] - m) * c) / l;
+            const double ns = (me ? 0.0 : sc[slot]) + p;
+            sc[slot] = ns;
+            const int pos = me ? a.t : s_meta[4 + slot];
+            if (a.select && pos <= lim && (ns < bkey || (ns == bkey && pos < bpos))) {
+                bkey = ns;
+                bpos = pos;
+                bslot = slot;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double k2 = __shfl_xor(bkey, o);
+            const int p2 = __shfl_xor(bpos, o);
+            const int s2 = __shfl_xor(bslot, o);
+            if (k2 < bkey || (k2 == bkey && p2 < bpos)) {
+                bkey = k2;
+                bpos = p2;
+                bslot = s2;
+            }
+        }
+        if (wl == 0) {
+            int32_t* meta = a.meta + (size_t)lane * a.meta_stride;
+            meta[4 + fslot] = a.t;
+            int chosen = -1;
+            if (a.select && bslot >= 0) {
+                chosen = bpos;
+                meta[0] = bslot;
+            }
+            if (a.trace) {
+                a.trace[2 * lane] = chosen;
+                a.trace[2 * lane + 1] = -1;
+            }
         }
     }
 }
@@ -396,14 +521,34 @@ hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t
     constexpr int TPR = D / Traits<T>::EPT;
     const int G = waves * (64 / TPR);
     dim3 grid(a.lanes), block(64 * waves);
-    if (mode == MODE_SPARSE) {
-        const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;
-        if (U * G <= a.L_p + a.n_sink)
-            hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
-    } else {
-        hipLaunchKernelGGL((decode_kernel<T, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
+    switch (mode) {
+        case MODE_SPARSE: {
+            const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;
+            if (U * G <= a.L_p + a.n_sink)
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
+            else
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
+            break;
+        }
+        case MODE_DENSE:
+            hipLaunchKernelGGL((decode_kernel<T, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
+            break;
+        case MODE_TOVA: {
+            const size_t lds = (size_t)a.meta_stride * 4;
+            if (U * G <= a.L_p)
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_TOVA, U, true>), grid, block, lds, s, a);
+            else
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_TOVA, U, false>), grid, block, lds, s, a);
+            break;
+        }
+        default: {  // MODE_H2O: slot metadata, then one fp64 logit per attended row
+            const size_t lds = (size_t)a.meta_stride * 4 + (size_t)(a.L_p + a.N_cache) * 8;
+            if (U * G <= a.L_p)
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_H2O, U, true>), grid, block, lds, s, a);
+            else
+                hipLaunchKernelGGL((decode_kernel<T, D, MODE_H2O, U, false>), grid, block, lds, s, a);
+            break;
+        }
     }
     return hipGetLastError();
 }

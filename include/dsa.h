@@ -88,6 +88,66 @@ size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int hea
 int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
                    int dtype, void* d_workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * KV-selection policies.  DIAGONAL and DIAGONAL_SINK4 are Algorithm 1 and its
+ * Diagonal+Sink4 variant (the states dsa_state_init makes).  The others are
+ * the baselines the pages compare against, under the same budget accounting
+ * (prompt always attended; N_att decode entries attended per step once that
+ * many exist, the current token included):
+ *   SLIDING_WINDOW - the N_att most recent decode positions (Section 2.3 (2));
+ *   STREAMING_LLM  - decode positions 0..3 as attention sinks plus the
+ *                    N_att - 4 most recent ones (Section 2.3 (2); Section 5.1
+ *                    "Sparse KV baselines": the first 4 decode tokens are the
+ *                    sinks since the prompt is kept whole);
+ *   TOVA           - a cache of N_att entries; once step t has filled it, the
+ *                    entry with the lowest logit q_t . k (the lowest score of
+ *                    this step's query; the current token included) leaves
+ *                    it, the lowest position among equals (Section 2.3 (3));
+ *   H2O            - a cache of N_att entries whose N_r most recent positions
+ *                    are protected; every entry accumulates its softmax
+ *                    probability (over prompt + cache) at each step it is
+ *                    attended, and once step t has filled the cache the
+ *                    unprotected entry with the lowest accumulated score
+ *                    leaves it, the lowest position among equals (Section 2.3
+ *                    (3)).  Scores and their probabilities are fp64.
+ * SLIDING_WINDOW and STREAMING_LLM run as Algorithm 1 with a ring of N_att
+ * entries (it never selects); TOVA and H2O run on their own kernel modes.
+ */
+typedef enum {
+    DSA_POLICY_DIAGONAL = 0,
+    DSA_POLICY_DIAGONAL_SINK4 = 1,
+    DSA_POLICY_SLIDING_WINDOW = 2,
+    DSA_POLICY_STREAMING_LLM = 3,
+    DSA_POLICY_TOVA = 4,
+    DSA_POLICY_H2O = 5
+} dsa_policy;
+
+/* Largest L_p + N_att of an H2O state (one fp64 logit per attended row lives in LDS). */
+#define DSA_MAX_H2O_ROWS 4096
+
+/*
+ * Device workspace bytes of a state of the given policy; 0 when the parameters
+ * are invalid (same rules as dsa_policy_state_init).  N_r is the ring (DIAGONAL,
+ * DIAGONAL_SINK4), must equal N_att (SLIDING_WINDOW, STREAMING_LLM, TOVA), or is
+ * H2O's protected recent count in [1, N_att - 1].  TOVA / H2O workspaces hold
+ * per lane L_p + N_att cache rows, the slot metadata (N_att + 4 int32) and, for
+ * H2O, N_att fp64 scores.
+ */
+size_t dsa_policy_workspace_bytes(int policy, int batch, int L_p, int N_r, int N_att, int heads, int head_dim,
+                                  int dtype);
+
+/*
+ * Create a state of the given policy; otherwise as dsa_state_init (no sink
+ * argument: the policy fixes it).  N_att <= DSA_MAX_ATTEND for TOVA and H2O,
+ * L_p + N_att <= DSA_MAX_H2O_ROWS for H2O.  The state takes the dsa_ calls:
+ * dsa_append_prompt, dsa_append_kv, dsa_decode_step, dsa_read_state.  For TOVA
+ * and H2O the trace of dsa_decode_step is (position that leaves the cache after
+ * this step or -1, -1), and dsa_read_state lists N_att offsets per lane (the
+ * cached entries the next step attends, with offset 0 for the next token).
+ */
+int dsa_policy_state_init(dsa_state** out, int policy, int batch, int L_p, int N_r, int N_att, int heads,
+                          int head_dim, int dtype, void* d_workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Change the stream later calls enqueue on. */
 int dsa_set_stream(dsa_state* st, void* hip_stream);
 

@@ -33,15 +33,22 @@ def device_inputs(w, layer, T, dev):
     return q, k, v, kp, vp
 
 
-def run_sparse(w, inputs, T, dev, waves=0, read_every=0):
+def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None):
     """T steps of one layer.  Returns out [T][B][H][D] (device), trace [T][B][H][2]
-    (host) and, with read_every > 0, {t: (offsets, counts)} read after step t."""
+    (host) and, with read_every > 0, {t: (offsets, counts)} read after step t.
+    With `policy` the state comes from dsa_policy_state_init (N_r defaults to w.N_r)."""
     q, k, v, kp, vp = inputs
     B, H, D = w.batch, w.heads, w.head_dim
-    nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes, stream)
+    if policy is None:
+        nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes, stream)
+    else:
+        n_r = w.N_r if N_r is None else N_r
+        nbytes = dsa.dsa_policy_workspace_bytes(policy, B, w.L_p, n_r, w.N_att, H, D, w.dtype)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        st = dsa.dsa_policy_state_init(policy, B, w.L_p, n_r, w.N_att, H, D, w.dtype, ws, nbytes, stream)
     dsa.dsa_set_waves(st, waves)
     out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
     trace = torch.empty((T, B, H, 2), dtype=torch.int32, device=dev)
