@@ -49,6 +49,7 @@ struct dsa_state {
     char* ws;
     size_t ws_bytes;
     size_t list_off;
+    size_t ring_off;  // sparse: byte offset of the ring region
     hipStream_t stream;
     int t;
     int prompt_done;
@@ -331,10 +332,11 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->N_rw = N_r - sink;
     st->N_attw = N_att - sink;
     st->list_stride = list_stride_for(N_att - sink);
-    st->lane_rows = (long long)L_p + N_r;
+    st->lane_rows = L_p;  // prompt region [lanes][L_p]; the ring region [N_r][lanes] follows it
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
-    st->list_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    st->ring_off = (size_t)st->lanes * (size_t)L_p * 2 * (size_t)head_dim * elem_size(dtype);
+    st->list_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
     st->stream = static_cast<hipStream_t>(hip_stream);
     *out = st;
     return DSA_OK;
@@ -421,6 +423,7 @@ int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) 
     const int t = st->t, S = st->S, N_rw = st->N_rw, N_attw = st->N_attw;
     const int tw = t - S;  // step inside the non-sink sequence
     a.list = reinterpret_cast<int16_t*>(st->ws + st->list_off);
+    a.ring = st->ws + st->ring_off;
     a.trace = trace;
     a.S = S;
     a.N_rw = N_rw;

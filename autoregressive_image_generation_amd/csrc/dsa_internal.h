@@ -15,8 +15,16 @@ enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_TOVA = 2, MODE_H2O = 3 };
 // Everything one decode launch needs.  Host-computed per step: all lanes of a
 // state share t, so the phase logic of Algorithm 1 (page 4, Section 4) is
 // resolved here once and the kernel only sees its consequences.
+// Cache layout.  A row is K (D elements) then V (D elements).  Dense and
+// TOVA / H2O states: [lanes][lane_rows] rows (prompt rows, then decode rows or
+// slots).  Sparse states: the prompt region [lanes][L_p] rows at kv, then the
+// ring region at `ring`: [N_r][lanes] rows, i.e. ring index i (sinks 0..S-1,
+// then the window slots) of every lane side by side.  A step appends the same
+// ring index in every lane, so its writes form one contiguous block, and the
+// window reads of all lanes fall into the ring rows of a few indices.
 struct DecodeArgs {
-    const void* kv;        // cache base: [lanes][lane_rows][2][D] (K row then V row)
+    const void* kv;        // cache base (see above); lane_rows = L_p for sparse states
+    const void* ring;      // sparse: ring region [N_r][lanes] rows
     int16_t* list;         // sparse: [lanes][list_stride] attended window offsets (t - position)
     const void* q;         // [lanes][D]
     const void* k_new;     // [lanes][D], the step's appended key
@@ -36,7 +44,7 @@ struct DecodeArgs {
     int select;            // sparse: 1 if this step picks a new skip entry
     int add_off;           // sparse: offset entering the list for step t+1, or -1
     int base;              // sparse: (t - S) mod N_rw, ring index of the current token
-    int self_row;          // cache row (after the prompt rows) the appended K/V goes to
+    int self_row;          // sparse: ring index the appended K/V goes to; dense: decode row
     int evicted;           // sparse: position evicted at this step, or -1
     double scale_log2e;    // log2(e) / sqrt(D)
     // TOVA / H2O (slot cache; cache rows L_p .. L_p + N_cache - 1 are the slots)

@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     auto row_src = [&](int r, const T*& kr, const T*& vr, int& d) {
         const bool listed = r >= win0;
         bool self;
-        int row;
+        const T* base;
         d = -1;
         if constexpr (MODE == MODE_SPARSE) {
             // Offsets are written only by this kernel and lie in [0, N_rw);
@@ -215,20 +215,22 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
             slot += slot < 0 ? a.N_rw : 0;
             // the current token is a listed entry (offset 0) or, while t < S, a sink
             self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
-            row = listed ? a.L_p + a.S + slot : r;
+            const int ri = listed ? a.S + slot : max(r - a.L_p, 0);  // ring index of a sink or window entry
+            const T* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * ROW;
+            const T* rrow = reinterpret_cast<const T*>(a.ring) + ((size_t)ri * a.lanes + lane) * ROW;
+            base = r < a.L_p ? prow : rrow;
             d = listed ? dl : -1;
         } else if constexpr (MODE == MODE_DENSE) {
             self = r >= a.L_p && r - a.L_p == a.t;
-            row = r;
+            base = lane_kv + (size_t)r * ROW;
         } else {
             const int j = max(r - win0, 0);
             const bool me = j == a.n_occ;
             const int slot = min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
             self = listed && me;
-            row = listed ? a.L_p + slot : r;
+            base = lane_kv + (size_t)(listed ? a.L_p + slot : r) * ROW;
             d = listed ? (me ? 0 : a.t - s_meta[4 + slot]) : -1;
         }
-        const T* base = lane_kv + (size_t)row * ROW;
         kr = self ? k_self : base;
         vr = self ? v_self : base + D;
     };
@@ -335,10 +337,12 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     // is the free slot); the current token itself is read from k_new / v_new.
     // Loaded at the start, stored here, so it adds no latency of its own.
     if (tid < CH) {
-        const int self_row = SLOTS ? fslot : a.self_row;
-        T* dst = const_cast<T*>(lane_kv) + (size_t)(a.L_p + self_row) * ROW + (tid / (CH / 2)) * D +
-                 (tid % (CH / 2)) * EPT;
-        *reinterpret_cast<uint4*>(dst) = ax;
+        T* row;
+        if constexpr (MODE == MODE_SPARSE)
+            row = const_cast<T*>(reinterpret_cast<const T*>(a.ring)) + ((size_t)a.self_row * a.lanes + lane) * ROW;
+        else
+            row = const_cast<T*>(lane_kv) + (size_t)(a.L_p + (SLOTS ? fslot : a.self_row)) * ROW;
+        *reinterpret_cast<uint4*>(row + (tid / (CH / 2)) * D + (tid % (CH / 2)) * EPT) = ax;
     }
 
     // Merge the groups of this wavefront (butterfly over lanes TPR apart).

@@ -35,9 +35,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC = {
     # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
     # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "5ebed0da750676a7"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "94aec6bd99f46058"},
     # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.5e6, "kernel_sha256_16": "5ebed0da750676a7"},
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.5e6, "kernel_sha256_16": "94aec6bd99f46058"},
 }
 
 
@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
+    p.add_argument("--no-policies", action="store_true",
+                   help="skip the baseline policies (SlidingWindow, StreamingLLM, TOVA, H2O) at equal N_att")
     p.add_argument("--summarize-trace", metavar="CSV",
                    help="only summarise a rocprofv3 run_kernel_trace.csv by kernel and launch shape, then exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -95,6 +97,40 @@ def sparse_bytes_per_head_step(w, t):
     n_sink = min(t + 1, S)
     rows = w.L_p + n_sink + n_list
     return rows * E + E + w.head_dim * es + 4 * w.head_dim + 2 * n_list
+
+
+POLICY_NAMES = ["diagonal", "diagonal_sink4", "sliding_window", "streaming_llm", "tova", "h2o"]
+
+
+def policy_n_r(w, policy):
+    """N_r argument of each policy at workload w: the ring for the diagonal
+    policies, the cache size for SlidingWindow / StreamingLLM / TOVA, and for
+    H2O the protected recent count (half the budget, rounded up)."""
+    if policy <= 1:
+        return w.N_r
+    return w.N_att - w.N_att // 2 if policy == 5 else w.N_att
+
+
+def policy_bytes_per_head_step(w, policy, t):
+    """Algorithmic HBM bytes of one lane at step t under a policy.  Position
+    policies are Algorithm 1 states (ring = N_att); TOVA / H2O read the attended
+    slot rows, their slot metadata (4 + min(t, N_att) int32, 16-byte chunks) and
+    write the new slot position and free slot (8 B); H2O also reads the cached
+    entries' fp64 scores and writes them back with the new token's."""
+    import synth
+
+    if policy in (0, 1):
+        return sparse_bytes_per_head_step(w.with_(sink=4 if policy == 1 else 0), t)
+    if policy in (2, 3):
+        return sparse_bytes_per_head_step(w.with_(N_r=w.N_att, sink=4 if policy == 3 else 0), t)
+    es = 2 if w.dtype == synth.BF16 else 4
+    E = 2 * w.head_dim * es
+    n = min(t + 1, w.N_att)
+    n_meta = 4 + min(t, w.N_att)
+    b = (w.L_p + n) * E + E + w.head_dim * es + 4 * w.head_dim + (n_meta + 3) // 4 * 16 + 8
+    if policy == 5:
+        b += 8 * (n - 1) + 8 * n
+    return b
 
 
 def dense_bytes_per_head_step(w, t):
@@ -167,7 +203,7 @@ class SparseModel:
     independent, so one's launch can overlap another's.
     """
 
-    def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1):
+    def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1, policy=None):
         import torch
 
         import autoregressive_image_generation_amd as dsa
@@ -178,8 +214,13 @@ class SparseModel:
             raise ValueError("batch %d does not split into %d micro-batches" % (self.B, streams))
         self.S = streams
         self.Bc = self.B // streams
-        self.nbytes = dsa.dsa_state_workspace_bytes(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink,
-                                                    w.dtype)
+        self.policy = policy
+        if policy is None:
+            self.nbytes = dsa.dsa_state_workspace_bytes(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink,
+                                                        w.dtype)
+        else:
+            self.nbytes = dsa.dsa_policy_workspace_bytes(policy, self.Bc, w.L_p, policy_n_r(w, policy), w.N_att,
+                                                         w.heads, w.head_dim, w.dtype)
         self.ws = [[torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
                    for _ in range(streams)]
         self.out = torch.empty((self.B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
@@ -189,6 +230,9 @@ class SparseModel:
 
     def _init_state(self, ws, stream):
         w = self.w
+        if self.policy is not None:
+            return self.dsa.dsa_policy_state_init(self.policy, self.Bc, w.L_p, policy_n_r(w, self.policy), w.N_att,
+                                                  w.heads, w.head_dim, w.dtype, ws, self.nbytes, stream)
         return self.dsa.dsa_state_init(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink, w.dtype, ws,
                                        self.nbytes, stream)
 
@@ -565,6 +609,21 @@ def main():
         log("dense b%d: %.1f ms per decode; sparse b%d %.1f ms -> %.2fx" % (db, dsec * 1e3, db, ssec * 1e3,
                                                                            dsec / ssec))
         del dense, sparse_b
+
+    if not args.no_policies:
+        pol = []
+        for policy in range(6):
+            if policy == 1 and w.N_att <= 4 or policy == 3 and w.N_att <= 4:
+                continue
+            m = SparseModel(w, inputs, layers, dev, waves, streams=S, policy=policy)
+            s_p, _ = time_decodes(m, args.steps, args.warmup, dev)
+            b = sum(policy_bytes_per_head_step(w, policy, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+            pol.append({"policy": POLICY_NAMES[policy], "N_r": policy_n_r(w, policy), "N_att": w.N_att,
+                        "value": head_steps / s_p, "ms_per_step": s_p * 1e3, "hbm_gbs": b / s_p / 1e9,
+                        "workspace_gb": m.nbytes * S * layers / 1e9})
+            log("policy %s: %.1f ms per decode, %.0f GB/s" % (POLICY_NAMES[policy], s_p * 1e3, b / s_p / 1e9))
+            del m
+        result["policies"] = pol
 
     if args.sweep:
         sweep = []
