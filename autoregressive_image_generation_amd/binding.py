@@ -31,12 +31,14 @@ _SIGNATURES = {
     "dsa_append_prompt": (_c_int, [_P, _P, _P]),
     "dsa_append_kv": (_c_int, [_P, _P, _P]),
     "dsa_decode_step": (_c_int, [_P, _P, _P, _P]),
+    "dsa_append_decode_step": (_c_int, [_P, _P, _P, _P, _P, _P]),
     "dsa_read_state": (_c_int, [_P, _P, _P, _P]),
     "dense_state_workspace_bytes": (_c_size, [_c_int] * 6),
     "dense_state_init": (_c_int, [ctypes.POINTER(_P)] + [_c_int] * 6 + [_P, _c_size, _P]),
     "dense_append_prompt": (_c_int, [_P, _P, _P]),
     "dense_append_kv": (_c_int, [_P, _P, _P]),
     "dense_decode_step": (_c_int, [_P, _P, _P]),
+    "dense_append_decode_step": (_c_int, [_P, _P, _P, _P, _P]),
     "dsa_set_waves": (_c_int, [_P, _c_int]),
     "dsa_state_step": (_c_int, [_P]),
     "dsa_state_destroy": (_c_int, [_P]),
@@ -170,6 +172,10 @@ def dsa_decode_step(st, q_t, out, trace=None):
     return _check(library().dsa_decode_step(st, _ptr(q_t), _ptr(out), _ptr(trace)))
 
 
+def dsa_append_decode_step(st, k_t, v_t, q_t, out, trace=None):
+    return _check(library().dsa_append_decode_step(st, _ptr(k_t), _ptr(v_t), _ptr(q_t), _ptr(out), _ptr(trace)))
+
+
 def dsa_read_state(st):
     """Returns (t, offsets [lanes][N_att - sink] int16 padded with -1, counts [lanes] int32).
 
@@ -202,6 +208,10 @@ def dense_append_kv(st, k_t, v_t):
 
 def dense_decode_step(st, q_t, out):
     return _check(library().dense_decode_step(st, _ptr(q_t), _ptr(out)))
+
+
+def dense_append_decode_step(st, k_t, v_t, q_t, out):
+    return _check(library().dense_append_decode_step(st, _ptr(k_t), _ptr(v_t), _ptr(q_t), _ptr(out)))
 
 
 def dsa_set_waves(st, waves_per_lane):

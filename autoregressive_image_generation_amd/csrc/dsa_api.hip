@@ -449,6 +449,17 @@ int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) 
     return DSA_OK;
 }
 
+int dsa_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, const void* q_t, float* out,
+                           int32_t* trace) {
+    int rc = dsa_append_kv(st, k_t, v_t);
+    if (rc) return rc;
+    rc = dsa_decode_step(st, q_t, out, trace);
+    if (rc) {  // leave the state as it was: no row recorded
+        st->pend_k = st->pend_v = nullptr;
+    }
+    return rc;
+}
+
 int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_t* h_count) {
     int rc = check_state(st, KIND_SPARSE, KIND_SCORE);
     if (rc) return rc;
@@ -549,6 +560,14 @@ int dense_decode_step(dsa_state* st, const void* q_t, float* out) {
     st->pend_k = st->pend_v = nullptr;
     st->t += 1;
     return DSA_OK;
+}
+
+int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, const void* q_t, float* out) {
+    int rc = dense_append_kv(st, k_t, v_t);
+    if (rc) return rc;
+    rc = dense_decode_step(st, q_t, out);
+    if (rc) st->pend_k = st->pend_v = nullptr;
+    return rc;
 }
 
 int dsa_set_waves(dsa_state* st, int waves_per_lane) {

@@ -266,29 +266,33 @@ class SparseModel:
         return self.dsa.library().dsa_decode_step
 
     def decode(self):
-        """All L_dec steps through all layers, in model order per micro-batch."""
+        """All L_dec steps through all layers, in model order per micro-batch: one
+        append-and-decode call per (step, layer, micro-batch)."""
         dsa, w = self.dsa, self.w
         q0 = self.inputs.layers[0]["q"]
         es = q0.element_size()
         step_bytes = q0[0].numel() * es
         chunk = self.Bc * w.heads * w.head_dim
-        ptrs = [(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr()) for x in self.inputs.layers]
         lib = dsa.library()
-        append = lib.dsa_append_kv if not isinstance(self, DenseModel) else lib.dense_append_kv
-        outs = [self.out.data_ptr() + c * chunk * 4 for c in range(self.S)]
-        layers = len(ptrs)
         dense = isinstance(self, DenseModel)
+        call = lib.dense_append_decode_step if dense else lib.dsa_append_decode_step
+        # per (layer, micro-batch), in launch order: state and its input / output addresses
+        plan = []
+        for layer, x in enumerate(self.inputs.layers):
+            for c in range(self.S):
+                off = c * chunk * es  # micro-batch c: contiguous in [B][H][D]
+                plan.append((self.states[c][layer], x["k"].data_ptr() + off, x["v"].data_ptr() + off,
+                             x["q"].data_ptr() + off, self.out.data_ptr() + c * chunk * 4))
         for t in range(w.L_dec):
-            for layer in range(layers):
-                qp, kp, vp = ptrs[layer]
-                for c in range(self.S):
-                    off = t * step_bytes + c * chunk * es  # micro-batch c of step t: contiguous in [B][H][D]
-                    st = self.states[c][layer]
-                    rc = append(st, kp + off, vp + off)
-                    if dense:
-                        rc |= lib.dense_decode_step(st, qp + off, outs[c])
-                    else:
-                        rc |= lib.dsa_decode_step(st, qp + off, outs[c], None)
+            o = t * step_bytes
+            if dense:
+                for st, kp, vp, qp, op in plan:
+                    rc = call(st, kp + o, vp + o, qp + o, op)
+                    if rc:
+                        raise dsa.DsaError(rc, dsa.dsa_last_error())
+            else:
+                for st, kp, vp, qp, op in plan:
+                    rc = call(st, kp + o, vp + o, qp + o, op, None)
                     if rc:
                         raise dsa.DsaError(rc, dsa.dsa_last_error())
 

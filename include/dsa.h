@@ -174,6 +174,14 @@ int dsa_append_kv(dsa_state* st, const void* k_t, const void* v_t);
 int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace);
 
 /*
+ * dsa_append_kv followed by dsa_decode_step, in one call (same arguments,
+ * checks and effects; nothing is recorded if either check fails).  For
+ * callers that enqueue many small launches and pay per call.
+ */
+int dsa_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, const void* q_t, float* out,
+                           int32_t* trace);
+
+/*
  * Copy the lane state to the host; synchronises the stream.  h_t receives the
  * index of the next step.  h_offsets ([batch*heads][N_att - sink], nullable)
  * receives, per lane, the window entries the next step will attend, as
@@ -200,6 +208,9 @@ int dense_append_kv(dsa_state* st, const void* k_t, const void* v_t);
 /* One dense decode step: out [batch][heads][head_dim] fp32.  Fails with
  * DSA_E_INVAL once L_max steps have run. */
 int dense_decode_step(dsa_state* st, const void* q_t, float* out);
+
+/* dense_append_kv followed by dense_decode_step, in one call. */
+int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, const void* q_t, float* out);
 
 /*
  * Workgroup size of the decode kernels, in 64-wide wavefronts per lane:

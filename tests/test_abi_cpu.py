@@ -141,6 +141,33 @@ def test_call_order_is_enforced_without_touching_the_device():
     dsa.dsa_state_destroy(st)
 
 
+def test_append_decode_step_checks_like_its_two_calls():
+    args = (1, 0, 16, 8, 2, 128, 4, 1)
+    st = dsa.dsa_state_init(*args, FAKE_WS, dsa.dsa_state_workspace_bytes(*args))
+    buf = FAKE_WS + (1 << 20)
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_decode_step(st, buf, buf, buf, buf)  # before the prompt
+    assert e.value.code == E_ORDER
+    dsa.dsa_append_prompt(st, None, None)
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_decode_step(st, buf + 8, buf, buf, buf)  # misaligned k_t
+    assert e.value.code == E_INVAL
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_decode_step(st, buf, buf, None, buf)  # the decode half fails ...
+    assert e.value.code == E_INVAL
+    dsa.dsa_append_kv(st, buf, buf)  # ... and leaves no row recorded
+    with pytest.raises(DsaError) as e:
+        dsa.dsa_append_decode_step(st, buf, buf, buf, buf)  # a row is already recorded
+    assert e.value.code == E_ORDER
+    assert dsa.dsa_state_step(st) == 0
+    dsa.dsa_state_destroy(st)
+    dst = dsa.dense_state_init(1, 0, 4, 2, 64, 1, FAKE_WS, 1 << 30)
+    with pytest.raises(DsaError) as e:
+        dsa.dense_append_decode_step(dst, buf, buf, buf, buf)
+    assert e.value.code == E_ORDER
+    dsa.dsa_state_destroy(dst)
+
+
 def test_null_state_and_handle():
     lib = dsa.library()
     assert lib.dsa_append_kv(None, None, None) == E_INVAL

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import autoregressive_image_generation_amd as dsa
 import oracle
 import synth
 from closed_form import attended_sets, falling_expected, rising_expected
@@ -99,6 +100,28 @@ def test_deterministic_across_runs():
     o2, t2, _ = run_sparse(w, ins, w.L_dec, DEV)
     assert torch.equal(o1, o2)
     np.testing.assert_array_equal(t1, t2)
+
+
+def test_append_decode_step_matches_the_two_calls():
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=2)
+    T = w.L_dec
+    ins = device_inputs(w, 0, T, DEV)
+    o1, t1, _ = run_sparse(w, ins, T, DEV)
+    q, k, v, kp, vp = ins
+    B, H, D = w.batch, w.heads, w.head_dim
+    nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes,
+                            torch.cuda.current_stream(DEV))
+    dsa.dsa_append_prompt(st, kp, vp)
+    o2 = torch.empty_like(o1)
+    t2 = torch.empty((T, B, H, 2), dtype=torch.int32, device=DEV)
+    for t in range(T):
+        dsa.dsa_append_decode_step(st, k[t], v[t], q[t], o2[t], t2[t])
+    torch.cuda.synchronize(DEV)
+    dsa.dsa_state_destroy(st)
+    assert torch.equal(o1, o2)
+    np.testing.assert_array_equal(t1, t2.cpu().numpy())
 
 
 # ------------------------------------------------------------ engineered closed forms on the GPU
