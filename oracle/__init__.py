@@ -20,7 +20,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "dsa_oracle.c"), os.path.join(_HERE, "baselines_oracle.c")]
+_SRCS = [os.path.join(_HERE, n) for n in ("dsa_oracle.c", "baselines_oracle.c", "mxfp8_oracle.c")]
 _LIB = os.path.join(_HERE, "_liboracle.so")
 
 _P = ctypes.c_void_p
@@ -51,6 +51,12 @@ def _load():
         lib.oracle_window_lane.argtypes = [ctypes.c_int] * 5 + [_P] * 8
         lib.oracle_score_lane.restype = ctypes.c_int
         lib.oracle_score_lane.argtypes = [ctypes.c_int] * 6 + [_P] * 12
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        lib.oracle_mxfp8_quantize.restype = ctypes.c_int
+        lib.oracle_mxfp8_quantize.argtypes = [_P, ctypes.c_int, _P, _P]
+        lib.oracle_mxfp8_dequantize.restype = ctypes.c_int
+        lib.oracle_mxfp8_dequantize.argtypes = [_P, _P, ctypes.c_int, _P]
         _lib = lib
     return _lib
 
@@ -185,6 +191,40 @@ def run_score_lane(policy, L_p, N_att, q, kp, vp, k, v, N_recent=0, follow=None,
     if scores:
         res["score"] = sc
     return res
+
+
+def e4m3_value(code):
+    """Value of an OCP E4M3 code (NaN for the two NaN codes)."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def quantize_mxfp8(x):
+    """MXFP8 E4M3 quantisation of the last axis (a multiple of 32) of x.
+
+    Returns (codes uint8, same shape as x; scales uint8, shape [..., n / 32])."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    if x.shape[-1] % 32:
+        raise ValueError("last axis must be a multiple of 32")
+    nb = x.size // 32
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // 32,), np.uint8)
+    _load().oracle_mxfp8_quantize(_ptr(x), nb, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_mxfp8(codes, scales):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if scales.size * 32 != codes.size:
+        raise ValueError("one scale per 32 codes")
+    out = np.empty(codes.shape, np.float64)
+    _load().oracle_mxfp8_dequantize(_ptr(codes), _ptr(scales), scales.size, _ptr(out))
+    return out
+
+
+def mxfp8_roundtrip(x):
+    """The values an MXFP8 cache holds for x (rows along the last axis)."""
+    return dequantize_mxfp8(*quantize_mxfp8(x))
 
 
 def lane_inputs(workload, layer, b, h, T=None):
