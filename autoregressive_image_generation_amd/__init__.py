@@ -9,6 +9,7 @@ autoregressive_image_generation_amd._build``).
 from .binding import (
     DSA_BF16,
     DSA_F32,
+    DSA_MXFP8,
     DSA_POLICY_DIAGONAL,
     DSA_POLICY_DIAGONAL_SINK4,
     DSA_POLICY_H2O,

@@ -15,7 +15,7 @@ import numpy as np
 
 from . import _build
 
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_MXFP8 = 0, 1, 2
 (DSA_POLICY_DIAGONAL, DSA_POLICY_DIAGONAL_SINK4, DSA_POLICY_SLIDING_WINDOW, DSA_POLICY_STREAMING_LLM, DSA_POLICY_TOVA,
  DSA_POLICY_H2O) = range(6)
 

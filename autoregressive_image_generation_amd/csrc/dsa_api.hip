@@ -63,7 +63,11 @@ struct dsa_state {
 
 namespace {
 
-size_t elem_size(int dtype) { return dtype == DSA_BF16 ? 2 : 4; }
+// Bytes of one cache row (K then V): plain elements, or MXFP8 codes plus the
+// 8-byte word of E8M0 block scales.
+size_t row_bytes(int D, int dtype) {
+    return dtype == DSA_MXFP8 ? (size_t)2 * D + 8 : (size_t)2 * D * (dtype == DSA_BF16 ? 2 : 4);
+}
 
 // Per-lane list entries, padded so every lane's list starts on 16 bytes.
 int list_stride_for(int n) { return (n + 7) / 8 * 8; }
@@ -76,7 +80,8 @@ int check_common(int batch, int L_p, int heads, int head_dim, int dtype) {
     if (heads < 1) return fail(DSA_E_INVAL, "heads must be >= 1 (got %d)", heads);
     if (head_dim != 64 && head_dim != 128) return fail(DSA_E_INVAL, "head_dim must be 64 or 128 (got %d)", head_dim);
     if (L_p < 0) return fail(DSA_E_INVAL, "L_p must be >= 0 (got %d)", L_p);
-    if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_E_INVAL, "dtype must be DSA_F32 or DSA_BF16");
+    if (dtype != DSA_F32 && dtype != DSA_BF16 && dtype != DSA_MXFP8)
+        return fail(DSA_E_INVAL, "dtype must be DSA_F32, DSA_BF16 or DSA_MXFP8");
     if ((long long)batch * heads > (1ll << 30)) return fail(DSA_E_INVAL, "batch * heads too large");
     return 0;
 }
@@ -95,7 +100,7 @@ int check_sparse(int batch, int L_p, int N_r, int N_att, int heads, int head_dim
 }
 
 size_t kv_bytes(long long lanes, long long lane_rows, int D, int dtype) {
-    return align_up((size_t)lanes * (size_t)lane_rows * 2 * (size_t)D * elem_size(dtype));
+    return align_up((size_t)lanes * (size_t)lane_rows * row_bytes(D, dtype));
 }
 
 int check_workspace(void* ws, size_t have, size_t need) {
@@ -128,7 +133,8 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // stays at 8 wavefronts or fewer (16 was slower at every measured shape).
 int choose_waves(const dsa_state* st, long long rows) {
     if (st->waves) return st->waves;
-    const int gpw = 64 / (st->D / (16 / (int)elem_size(st->dtype)));
+    const int ept = st->dtype == DSA_F32 ? 4 : 8;  // elements of K (and of V) per thread
+    const int gpw = 64 / (st->D / ept);
     int w = 1;
     while (w < 8 && (long long)st->lanes * (2 * w) < 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;
     return w;
@@ -335,7 +341,7 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->lane_rows = L_p;  // prompt region [lanes][L_p]; the ring region [N_r][lanes] follows it
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
-    st->ring_off = (size_t)st->lanes * (size_t)L_p * 2 * (size_t)head_dim * elem_size(dtype);
+    st->ring_off = (size_t)st->lanes * (size_t)L_p * row_bytes(head_dim, dtype);
     st->list_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
     st->stream = static_cast<hipStream_t>(hip_stream);
     *out = st;

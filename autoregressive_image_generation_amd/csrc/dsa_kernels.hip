@@ -7,18 +7,32 @@
 // and H2O (the unprotected entry with the lowest accumulated score leaves).
 //
 // One workgroup per lane (one (sequence, head) of the layer), `waves` 64-wide
-// wavefronts.  A row of the cache is K (D elements) followed by V (D
-// elements); TPR = D * sizeof(T) / 16 threads cover one half-row with one
-// 16-byte load each, so a wavefront works on 64 / TPR rows at a time.  Each
-// such thread group keeps its own online-softmax state (m, l, acc) over the
-// rows it visits; groups merge through DPP / shuffles inside the wavefront and
-// through LDS across wavefronts.  Single-query decode does about one flop per
-// byte of KV, so the kernel is bound by HBM bandwidth; MFMA has no role.
+// wavefronts.  Each thread group of TPR threads holds one cache row at a time,
+// 8 (bf16, MXFP8) or 4 (fp32) elements of K and of V per thread; a wavefront
+// works on 64 / TPR rows at a time.  Each group keeps its own online-softmax
+// state (m, l, acc) over the rows it visits; groups merge through DPP /
+// shuffles inside the wavefront and through LDS across wavefronts.
+// Single-query decode does about one flop per byte of KV, so the kernel is
+// bound by HBM bandwidth; MFMA has no role.
 //
-// The raw logits q.k are accumulated in fp64: bf16 x bf16 products are exact
-// in fp64 and their sums nearly always are, so the argmin decision matches a
-// fp64 reference up to order-of-summation rounding far below the selection's
-// near-tie threshold.  The softmax runs in fp32 on the rounded logits.
+// The raw logits q.k are accumulated in fp64: the products of bf16 (or fp32,
+// or MXFP8) values are exact in fp64 and their sums nearly always are, so the
+// argmin decision matches a fp64 reference up to order-of-summation rounding
+// far below the selection's near-tie threshold.  The softmax runs in fp32 on
+// the rounded logits.
+//
+// Cache row formats:
+//   Plain<T>: K then V, D elements of T each (bf16 bit patterns or fp32); a
+//     thread's chunk is 16 bytes of K and 16 of V.
+//   Mx8 (the low-bit KV cache; Section 6 of the pages calls KV quantization
+//     stackable with the selection): MXFP8 of the OCP Microscaling v1.0
+//     format.  K codes (D bytes, E4M3), V codes (D bytes), then an 8-byte
+//     scale word: byte b the E8M0 scale of K block b, byte 4 + b that of V
+//     block b, blocks of 32 elements.  A thread's chunk is 8 codes of K, 8 of
+//     V and the scale word.  q and the appended K/V arrive in bf16; the
+//     appended row is quantised in the launch that appends it, and every
+//     decode row the attention reads, the current token's included, is the
+//     quantised one.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -31,16 +45,21 @@ constexpr float kNegBig = -1.0e30f;
 #endif
 constexpr int kRowsPerChunk = DSA_ROWS_PER_CHUNK;  // pipeline depth in rows per thread group
 
-template <typename T>
-struct Traits;
-template <>
-struct Traits<float> {
-    static constexpr int EPT = 4;  // elements per 16-byte chunk
-};
-template <>
-struct Traits<uint16_t> {  // bf16 bit patterns
-    static constexpr int EPT = 8;
-};
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Cache rows are read once per step and not again before every other layer
+// has streamed its own cache, so they bypass the caches' retention.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& x, float* f) {
@@ -59,19 +78,79 @@ __device__ __forceinline__ void unpack(const uint4& x, float* f) {
     }
 }
 
-__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// Cache rows are read once per step and not again before every other layer
-// has streamed its own cache, so they bypass the caches' retention.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_stream(const void* p) {
-#ifdef DSA_CACHED_ROWS
-    return *reinterpret_cast<const uint4*>(p);
-#else
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-#endif
+// ---------------------------------------------------------------- MXFP8
+// E4M3 codes -> floats (gfx950 converts OCP E4M3 in hardware, exactly).
+__device__ __forceinline__ void unpack_e4m3(const uint2& c, float* f) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+    const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    f[0] = a[0];
+    f[1] = a[1];
+    f[2] = b[0];
+    f[3] = b[1];
+    f[4] = d[0];
+    f[5] = d[1];
+    f[6] = e[0];
+    f[7] = e[1];
 }
+
+// 2^(s - 127) of an E8M0 byte (s = 0 is 2^-127, a float subnormal).
+__device__ __forceinline__ float e8m0_value(uint32_t s) { return __uint_as_float(s ? s << 23 : 0x00400000u); }
+
+// Shared exponent of a block, floor(log2(amax)) - 8 (8: the largest E4M3
+// exponent), clamped to the E8M0 range; -127 for an all-zero block.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    int e;
+    (void)frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1)
+    return min(max(e - 1 - 8, -127), 127);
+}
+
+// The E4M3 code nearest to y, ties to the even code, saturating at +-448.
+// |y| < 512 always holds for y = v / 2^X with the block's shared exponent X.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    const uint32_t ab = __float_as_uint(a);
+    int e = (int)(ab >> 23) - 127;
+    uint32_t q = (ab & 0x7fffffu) >> 20;
+    const uint32_t rest = ab & 0xfffffu;
+    q += (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ? 1u : 0u;
+    e += q == 8u ? 1 : 0;
+    q = q == 8u ? 0u : q;
+    const uint32_t normal = (e > 8 || (e == 8 && q == 7u)) ? 0x7eu : ((uint32_t)(e + 7) << 3) | q;
+    const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);  // multiples of 2^-9; 8 = code 0x08
+    return (a >= 0x1p-6f ? normal : sub) | sign;
+}
+
+// ---------------------------------------------------------------- row formats
+template <typename T>
+struct Plain {
+    using In = T;
+    static constexpr bool MX = false;
+    static constexpr int EPT = 16 / (int)sizeof(T);  // elements of K (and of V) per thread
+    template <int D>
+    static constexpr size_t row_bytes() {
+        return (size_t)2 * D * sizeof(T);
+    }
+    struct Chunk {
+        uint4 k, v;
+    };
+};
+
+struct Mx8 {
+    using In = uint16_t;  // q and the appended rows arrive in bf16
+    static constexpr bool MX = true;
+    static constexpr int EPT = 8;
+    template <int D>
+    static constexpr size_t row_bytes() {
+        return (size_t)2 * D + 8;
+    }
+    struct Chunk {
+        uint2 k, v, s;
+    };
+};
 
 // Exchange a double with the lane a DPP pattern names (both halves moved).
 template <int CTRL>
@@ -93,6 +172,13 @@ __device__ __forceinline__ double group_sum(double v) {
     if constexpr (TPR >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
     if constexpr (TPR >= 16) v += dpp_f64<0x140>(v);  // row_mirror
     if constexpr (TPR >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
+// Maximum over the 4 lanes of a quad (every lane ends with it).
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
     return v;
 }
 
@@ -130,16 +216,25 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+// Marks the current token's row in the MXFP8 row stream: it is taken from
+// registers after the merge, not read from the cache (d is the offset t -
+// position for window entries, -1 for prompt and sink rows).
+constexpr int kSelfOutOfStream = -2;
+
 // EARLY: every thread group's first U rows need no list or slot entry (U * G
 // <= number of prompt + sink rows), so they are requested before the lane's
 // index data has arrived.
-template <typename T, int D, int MODE, int U, bool EARLY>
+template <typename F, int D, int MODE, int U, bool EARLY>
 __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
-    constexpr int EPT = Traits<T>::EPT;
+    using T = typename F::In;
+    constexpr bool MX = F::MX;
+    constexpr int EPT = F::EPT;
     constexpr int TPR = D / EPT;          // threads per half-row
     constexpr int GPW = 64 / TPR;         // thread groups per wavefront
-    constexpr int ROW = 2 * D;            // elements per cache row
+    constexpr size_t RB = F::template row_bytes<D>();
     constexpr bool SLOTS = MODE == MODE_TOVA || MODE == MODE_H2O;
+    constexpr int IEPT = 16 / (int)sizeof(T);     // input elements per 16-byte chunk
+    constexpr int CH = 2 * D / IEPT;              // 16-byte chunks of an input K|V row
 
     // Dynamic LDS: the lane's index data, staged once per launch.  Sparse: the
     // attended window offsets (int16).  TOVA / H2O: the slot metadata (int32:
@@ -153,6 +248,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     __shared__ float s_acc[kMaxWaves][D];
     __shared__ double s_bs[kMaxWaves];
     __shared__ int s_bd[kMaxWaves], s_bj[kMaxWaves];
+    __shared__ int s_self_j;  // MXFP8 sparse: list index of the current token, -1 if not attended
 
     const int lane = blockIdx.x;
     const int tid = threadIdx.x;
@@ -163,9 +259,10 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     const int g = wave * GPW + wl / TPR;  // group index in the workgroup
     const int G = nwaves * GPW;
 
-    const T* lane_kv = reinterpret_cast<const T*>(a.kv) + (size_t)lane * (size_t)a.lane_rows * ROW;
-    const T* k_self = reinterpret_cast<const T*>(a.k_new) + (size_t)lane * D;
-    const T* v_self = reinterpret_cast<const T*>(a.v_new) + (size_t)lane * D;
+    const char* lane_kv = reinterpret_cast<const char*>(a.kv) + (size_t)lane * (size_t)a.lane_rows * RB;
+    const char* ring = reinterpret_cast<const char*>(a.ring);
+    const char* k_self = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k_new) + (size_t)lane * D);
+    const char* v_self = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v_new) + (size_t)lane * D);
 
     // Rows [0, R): prompt rows, then sinks (sparse) or cached decode positions
     // (dense), then from win0 on the listed window entries (sparse) or the
@@ -174,7 +271,6 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
                   : MODE == MODE_DENSE ? a.L_p + a.t + 1
                                        : a.L_p + a.n_occ + 1;
     const int win0 = MODE == MODE_SPARSE ? a.L_p + a.n_sink : MODE == MODE_DENSE ? R : a.L_p;
-    constexpr int CH = ROW * (int)sizeof(T) / 16;                // 16-byte chunks per row
 
     // Requests in the order their data is needed: the index data (16-byte
     // chunks; strides are padded to whole chunks), the query chunk, the
@@ -191,21 +287,23 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     }
     const uint4 qx = load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT);
     uint4 ax = make_uint4(0, 0, 0, 0);
-    if (tid < CH) ax = load16((tid < CH / 2 ? k_self : v_self) + (tid % (CH / 2)) * EPT);
+    if (tid < CH) ax = load16((tid < CH / 2 ? k_self : v_self) + (tid % (CH / 2)) * 16);
 
     // TOVA / H2O: the slot the current token takes (the one freed by the last
     // eviction, or the next empty one while the cache fills).
     int fslot = SLOTS && a.free_host >= 0 ? a.free_host : 0;
 
-    // Source of row r in [0, R).  Sparse: offset d = t - position of the
-    // listed entry, ring slot S + (t' - d) mod N_rw.  TOVA / H2O: the j-th
-    // occupied slot skips the free one; the last row is the current token.
-    // The current token is read from k_new / v_new.  Branch-free, so that the
-    // row loads below are straight-line code and every wait on them is exact.
-    auto row_src = [&](int r, const T*& kr, const T*& vr, int& d) {
+    // Source of row r in [0, R): the addresses of this thread's K and V
+    // chunks (and, MXFP8, of the row's scale word).  Sparse: offset d = t -
+    // position of the listed entry, ring index S + (t' - d) mod N_rw.  TOVA /
+    // H2O: the j-th occupied slot skips the free one; the last row is the
+    // current token.  The current token is read from k_new / v_new (plain
+    // rows) or taken out of the stream (MXFP8).  Branch-free, so that the row
+    // loads below are straight-line code and every wait on them is exact.
+    auto row_src = [&](int r, const char*& kr, const char*& vr, const char*& sr, int& d) {
         const bool listed = r >= win0;
         bool self;
-        const T* base;
+        const char* row;
         d = -1;
         if constexpr (MODE == MODE_SPARSE) {
             // Offsets are written only by this kernel and lie in [0, N_rw);
@@ -216,23 +314,44 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
             // the current token is a listed entry (offset 0) or, while t < S, a sink
             self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
             const int ri = listed ? a.S + slot : max(r - a.L_p, 0);  // ring index of a sink or window entry
-            const T* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * ROW;
-            const T* rrow = reinterpret_cast<const T*>(a.ring) + ((size_t)ri * a.lanes + lane) * ROW;
-            base = r < a.L_p ? prow : rrow;
+            const char* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * RB;
+            const char* rrow = ring + ((size_t)ri * a.lanes + lane) * RB;
+            row = r < a.L_p ? prow : rrow;
             d = listed ? dl : -1;
         } else if constexpr (MODE == MODE_DENSE) {
             self = r >= a.L_p && r - a.L_p == a.t;
-            base = lane_kv + (size_t)r * ROW;
+            row = lane_kv + (size_t)r * RB;
         } else {
             const int j = max(r - win0, 0);
             const bool me = j == a.n_occ;
             const int slot = min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
             self = listed && me;
-            base = lane_kv + (size_t)(listed ? a.L_p + slot : r) * ROW;
+            row = lane_kv + (size_t)(listed ? a.L_p + slot : r) * RB;
             d = listed ? (me ? 0 : a.t - s_meta[4 + slot]) : -1;
         }
-        kr = self ? k_self : base;
-        vr = self ? v_self : base + D;
+        if constexpr (MX) {
+            d = self ? kSelfOutOfStream : d;  // the row address stays a valid cache row
+            kr = row + sl * 8;
+            vr = row + D + sl * 8;
+            sr = row + 2 * D;
+        } else {
+            kr = (self ? k_self : row) + sl * 16;
+            vr = (self ? v_self : row + D * sizeof(T)) + sl * 16;
+            sr = nullptr;
+        }
+    };
+    auto load_row = [&](const char* kr, const char* vr, const char* sr) {
+        typename F::Chunk c;
+        if constexpr (MX) {
+            c.k = load8_stream(kr);
+            c.v = load8_stream(vr);
+            c.s = load8_stream(sr);
+        } else {
+            (void)sr;
+            c.k = load16_stream(kr);
+            c.v = load16_stream(vr);
+        }
+        return c;
     };
 
     // Rows of this group: r_k = g + k * G.  Every group of a wavefront runs the
@@ -241,20 +360,21 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     const int nk = (R - g + G - 1) / G;                      // rows this group consumes
     const int nkw = (R - wave * GPW + G - 1) / G;             // trip count of the wavefront
 
-    uint4 kx[U], vx[U];
+    typename F::Chunk cx[U];
     int dd[U];
     auto first_rows = [&]() {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const T* kr;
-            const T* vr;
-            row_src(min(g + u * G, R - 1), kr, vr, dd[u]);
-            kx[u] = load16_stream(kr + sl * EPT);
-            vx[u] = load16_stream(vr + sl * EPT);
+            const char *kr, *vr, *sr;
+            row_src(min(g + u * G, R - 1), kr, vr, sr, dd[u]);
+            cx[u] = load_row(kr, vr, sr);
         }
     };
     if constexpr (EARLY) first_rows();  // prompt rows only: no index data read
     if constexpr (MODE != MODE_DENSE) {
+        if constexpr (MX && MODE == MODE_SPARSE) {
+            if (tid == 0) s_self_j = -1;
+        }
         if (tid < nch) s_dyn16[tid] = lc0;
         if (tid + (int)blockDim.x < nch) s_dyn16[tid + blockDim.x] = lc1;
         for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_dyn16[c] = load16(idx16 + c);
@@ -282,22 +402,44 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     int best_d = -1, best_j = -1;
 
     // Consume one row: logit in fp64, argmin candidate, online softmax.  Rows
-    // past this group's share (k >= nk) enter with logit -inf and weight 0:
-    // selects instead of branches, so the loop below stays straight-line.
-    auto consume = [&](int k, const uint4& kq, const uint4& vq, int d) {
-        const bool valid = k < nk;
+    // past this group's share (k >= nk), and the out-of-stream current token
+    // of MXFP8, enter with logit -inf and weight 0: selects instead of
+    // branches, so the loop below stays straight-line.
+    auto consume = [&](int k, const typename F::Chunk& ch, int d) {
         const int r = g + k * G;
+        int jj = r - win0;  // sparse: list index; TOVA: the slot (below)
+        if constexpr (MODE == MODE_TOVA) jj = jj == a.n_occ ? fslot : jj + (jj >= fslot ? 1 : 0);
         float kf[EPT], vf[EPT];
-        unpack<T>(kq, kf);
-        unpack<T>(vq, vf);
+        bool valid = k < nk;
+        double kscale = 1.0;
+        float vscale = 1.0f;
+        if constexpr (MX) {
+            if constexpr (MODE == MODE_SPARSE) {
+                // the list index of the current token; a sink (t < S, never a
+                // selection step) records 0 just to mark it attended
+                if (valid && d == kSelfOutOfStream && sl == 0) s_self_j = max(jj, 0);
+            }
+            valid = valid && d != kSelfOutOfStream;
+            // a row that does not count may be an unwritten cache row (the
+            // current token's placeholder): zero its bytes so that no NaN code
+            // reaches the accumulator through a zero weight
+            const uint32_t keep = valid ? 0xffffffffu : 0u;
+            unpack_e4m3(make_uint2(ch.k.x & keep, ch.k.y & keep), kf);
+            unpack_e4m3(make_uint2(ch.v.x & keep, ch.v.y & keep), vf);
+            const int b = sl >> 2;  // this thread's 8 elements lie in block b of 32
+            kscale = (double)e8m0_value((ch.s.x & keep) >> (8 * b) & 0xffu);
+            vscale = e8m0_value((ch.s.y & keep) >> (8 * b) & 0xffu);
+        } else {
+            unpack<T>(ch.k, kf);
+            unpack<T>(ch.v, vf);
+        }
         double part = 0.0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
+        if constexpr (MX) part *= kscale;  // a power of two: exact
         const double s = group_sum<TPR>(part);
         if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
             const bool cand = valid && a.select && d >= 0 && better(s, d, best_s, best_d);
-            int jj = r - win0;  // sparse: list index
-            if constexpr (MODE == MODE_TOVA) jj = jj == a.n_occ ? fslot : jj + (jj >= fslot ? 1 : 0);  // slot
             best_s = cand ? s : best_s;
             best_d = cand ? d : best_d;
             best_j = cand ? jj : best_j;
@@ -310,8 +452,9 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         const float c = __builtin_amdgcn_exp2f(sm.m - mn);
         const float p = __builtin_amdgcn_exp2f(x - mn);
         sm.l = sm.l * c + p;
+        const float pv = MX ? p * vscale : p;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + p * vf[e];
+        for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + pv * vf[e];
         sm.m = mn;
     };
 
@@ -321,28 +464,57 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     for (; k0 + U < nkw; k0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            consume(k0 + u, kx[u], vx[u], dd[u]);
-            const T* kr;
-            const T* vr;
-            row_src(min(g + (k0 + u + U) * G, R - 1), kr, vr, dd[u]);
-            kx[u] = load16_stream(kr + sl * EPT);
-            vx[u] = load16_stream(vr + sl * EPT);
+            consume(k0 + u, cx[u], dd[u]);
+            const char *kr, *vr, *sr;
+            row_src(min(g + (k0 + u + U) * G, R - 1), kr, vr, sr, dd[u]);
+            cx[u] = load_row(kr, vr, sr);
         }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) consume(k0 + u, kx[u], vx[u], dd[u]);
+    for (int u = 0; u < U; ++u) consume(k0 + u, cx[u], dd[u]);
 
     // Append: the new K/V row goes to its cache row.  Nothing this launch
     // reads lives there (it is empty, holds the entry evicted at this step, or
-    // is the free slot); the current token itself is read from k_new / v_new.
-    // Loaded at the start, stored here, so it adds no latency of its own.
-    if (tid < CH) {
-        T* row;
-        if constexpr (MODE == MODE_SPARSE)
-            row = const_cast<T*>(reinterpret_cast<const T*>(a.ring)) + ((size_t)a.self_row * a.lanes + lane) * ROW;
-        else
-            row = const_cast<T*>(lane_kv) + (size_t)(a.L_p + (SLOTS ? fslot : a.self_row)) * ROW;
-        *reinterpret_cast<uint4*>(row + (tid / (CH / 2)) * D + (tid % (CH / 2)) * EPT) = ax;
+    // is the free slot); the current token itself is read from k_new / v_new
+    // (plain) or from the registers below (MXFP8).  Loaded at the start,
+    // stored here, so it adds no latency of its own.
+    char* dst_row;
+    if constexpr (MODE == MODE_SPARSE)
+        dst_row = const_cast<char*>(ring) + ((size_t)a.self_row * a.lanes + lane) * RB;
+    else
+        dst_row = const_cast<char*>(lane_kv) + (size_t)(a.L_p + (SLOTS ? fslot : a.self_row)) * RB;
+    uint2 qcode = make_uint2(0, 0);  // MXFP8: this lane's 8 codes of the new row (lanes < CH of wave 0)
+    uint32_t qscale = 0;             // and the E8M0 scale of its block
+    if constexpr (MX) {
+        if (wave == 0) {
+            // lanes 0 .. CH/2-1 hold K, CH/2 .. CH-1 hold V, 8 elements each;
+            // a block of 32 is a quad of lanes
+            float xf[8];
+            unpack<uint16_t>(ax, xf);
+            float am = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xf[e]));
+            const int X = mx_shared_exp(quad_max(am));
+            uint32_t c[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) c[e] = e4m3_rne_sat(ldexpf(xf[e], -X));
+            qcode = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+            qscale = (uint32_t)(X + 127);
+            // the scale word: K block b at byte b, V block b at byte 4 + b
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b) {
+                w0 |= (uint32_t)__shfl((int)qscale, 4 * b) << (8 * b);
+                w1 |= (uint32_t)__shfl((int)qscale, CH / 2 + 4 * b) << (8 * b);
+            }
+            if (tid < CH) {
+                const int off = tid < CH / 2 ? 8 * tid : D + 8 * (tid - CH / 2);
+                *reinterpret_cast<uint2*>(dst_row + off) = qcode;
+            }
+            if (tid == 0) *reinterpret_cast<uint2*>(dst_row + 2 * D) = make_uint2(w0, w1);
+        }
+    } else {
+        if (tid < CH) *reinterpret_cast<uint4*>(dst_row + tid * 16) = ax;
     }
 
     // Merge the groups of this wavefront (butterfly over lanes TPR apart).
@@ -381,12 +553,51 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (wave != 0) return;
 
+    // MXFP8: the current token's row, quantised above, enters after the merge
+    // of all other rows, in the lanes of wave 0's first group (its K half is
+    // in lanes 0 .. TPR-1, its V half in lanes TPR .. 2 TPR-1; CH = 2 TPR).
+    bool self_in = false;
+    int self_j = -1;
+    double self_s = 0.0;
+    float self_vf[EPT];
+    float self_vs = 1.0f;
+    if constexpr (MX) {
+        const uint2 vcode = make_uint2(__shfl((int)qcode.x, wl + TPR), __shfl((int)qcode.y, wl + TPR));
+        self_vs = e8m0_value((uint32_t)__shfl((int)qscale, wl + TPR));
+        if constexpr (MODE == MODE_SPARSE) {
+            self_j = s_self_j;
+            self_in = self_j >= 0;
+        } else {
+            self_in = true;
+            self_j = MODE == MODE_TOVA ? fslot : -1;
+        }
+        float kf[EPT];
+        unpack_e4m3(qcode, kf);
+        unpack_e4m3(vcode, self_vf);
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
+        self_s = group_sum<TPR>(part * (double)e8m0_value(qscale));
+    }
+
     if (wl < TPR) {
         for (int w = 1; w < nwaves; ++w) {
             float acc2[EPT];
 #pragma unroll
             for (int e = 0; e < EPT; ++e) acc2[e] = s_acc[w][sl * EPT + e];
             merge<EPT>(sm, acc, s_m[w], s_l[w], acc2);
+        }
+        if constexpr (MX) {
+            if (self_in) {
+                const float x = (float)(self_s * a.scale_log2e);
+                const float mn = fmaxf(sm.m, x);
+                const float c = __builtin_amdgcn_exp2f(sm.m - mn);
+                const float p = __builtin_amdgcn_exp2f(x - mn);
+                sm.l = sm.l * c + p;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + (p * self_vs) * self_vf[e];
+                sm.m = mn;
+            }
         }
         const float inv = 1.0f / sm.l;
         float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
@@ -402,6 +613,14 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
                 best_s = s_bs[w];
                 best_d = s_bd[w];
                 best_j = s_bj[w];
+            }
+        }
+        if constexpr (MX) {
+            // the current token as a candidate: offset 0
+            if (self_in && a.select && (best_d < 0 || better(self_s, 0, best_s, best_d))) {
+                best_s = self_s;
+                best_d = 0;
+                best_j = self_j;
             }
         }
         int chosen = -1;
@@ -440,11 +659,13 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         // (position <= t - n_recent) with the lowest score leaves, the lowest
         // position among equals.  Wave 0 does this for the lane.
         const double c = a.inv_sqrt_d;
+        const double self_logit = __shfl(self_s, 0);  // MXFP8: the current token's logit
+        auto logit = [&](int r) { return MX && r == R - 1 ? self_logit : s_logit[r]; };
         double m = -__builtin_inf();
-        for (int r = wl; r < R; r += 64) m = fmax(m, s_logit[r]);
+        for (int r = wl; r < R; r += 64) m = fmax(m, logit(r));
         m = wave_max(m);
         double l = 0.0;
-        for (int r = wl; r < R; r += 64) l += exp((s_logit[r] - m) * c);
+        for (int r = wl; r < R; r += 64) l += exp((logit(r) - m) * c);
         l = wave_sum(l);
         double* sc = a.score + (size_t)lane * a.score_stride;
         const int lim = a.t - a.n_recent;
@@ -453,7 +674,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         for (int j = wl; j <= a.n_occ; j += 64) {
             const bool me = j == a.n_occ;
             const int slot = me ? fslot : min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
-            const double p = exp((s_logit[win0 + j] - m) * c) / l;
+            const double p = exp((logit(win0 + j) - m) * c) / l;
             const double ns = (me ? 0.0 : sc[slot]) + p;
             sc[slot] = ns;
             const int pos = me ? a.t : s_meta[4 + slot];
@@ -490,27 +711,71 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     }
 }
 
-template <typename T, int D>
+// Prompt rows into the cache (plain: a copy; MXFP8: one block of 32 values
+// per thread, quantised), and the initial list entry {offset 0} of sink-free
+// sparse states.
+template <typename F, int D>
 __global__ void prompt_kernel(PromptArgs a) {
-    constexpr int EPT = Traits<T>::EPT;
-    constexpr int CPR = D / EPT;  // 16-byte chunks per half-row
-    const long long total = (long long)a.B * a.H * a.L_p * 2 * CPR;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long long)gridDim.x * blockDim.x) {
-        long long x = i;
-        const int c = (int)(x % CPR);
-        x /= CPR;
-        const int h = (int)(x % a.H);
-        x /= a.H;
-        const int half = (int)(x % 2);
-        x /= 2;
-        const int j = (int)(x % a.L_p);
-        const int b = (int)(x / a.L_p);
-        const T* src = reinterpret_cast<const T*>(half ? a.v_p : a.k_p) +
-                       (((size_t)b * a.L_p + j) * a.H + h) * D + c * EPT;
-        const size_t lane = (size_t)b * a.H + h;
-        T* dst = reinterpret_cast<T*>(a.kv) + (lane * (size_t)a.lane_rows + j) * 2 * D + half * D + c * EPT;
-        *reinterpret_cast<uint4*>(dst) = load16(src);
+    using T = typename F::In;
+    constexpr size_t RB = F::template row_bytes<D>();
+    if constexpr (F::MX) {
+        constexpr int NB = D / 32;  // blocks per half-row
+        const long long total = (long long)a.B * a.H * a.L_p * 2 * NB;
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+             i += (long long)gridDim.x * blockDim.x) {
+            long long x = i;
+            const int blk = (int)(x % NB);
+            x /= NB;
+            const int h = (int)(x % a.H);
+            x /= a.H;
+            const int half = (int)(x % 2);
+            x /= 2;
+            const int j = (int)(x % a.L_p);
+            const int b = (int)(x / a.L_p);
+            const T* src = reinterpret_cast<const T*>(half ? a.v_p : a.k_p) +
+                           (((size_t)b * a.L_p + j) * a.H + h) * D + blk * 32;
+            float v[32];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) unpack<uint16_t>(load16(src + 8 * c), v + 8 * c);
+            float am = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(v[e]));
+            const int X = mx_shared_exp(am);
+            uint32_t w[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                w[q] = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[q] |= e4m3_rne_sat(ldexpf(v[4 * q + e], -X)) << (8 * e);
+            }
+            const size_t lane = (size_t)b * a.H + h;
+            char* row = reinterpret_cast<char*>(a.kv) + (lane * (size_t)a.lane_rows + j) * RB;
+            uint4* dst = reinterpret_cast<uint4*>(row + half * D + blk * 32);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            row[2 * D + half * 4 + blk] = (char)(X + 127);
+        }
+    } else {
+        constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per half-row
+        const long long total = (long long)a.B * a.H * a.L_p * 2 * CPR;
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+             i += (long long)gridDim.x * blockDim.x) {
+            long long x = i;
+            const int c = (int)(x % CPR);
+            x /= CPR;
+            const int h = (int)(x % a.H);
+            x /= a.H;
+            const int half = (int)(x % 2);
+            x /= 2;
+            const int j = (int)(x % a.L_p);
+            const int b = (int)(x / a.L_p);
+            const char* src = reinterpret_cast<const char*>(half ? a.v_p : a.k_p) +
+                              (((size_t)b * a.L_p + j) * a.H + h) * D * sizeof(T) + c * 16;
+            const size_t lane = (size_t)b * a.H + h;
+            char* dst = reinterpret_cast<char*>(a.kv) + (lane * (size_t)a.lane_rows + j) * RB + half * D * sizeof(T) +
+                        c * 16;
+            *reinterpret_cast<uint4*>(dst) = load16(src);
+        }
     }
     if (a.list) {
         const int lanes = a.B * a.H;
@@ -519,74 +784,79 @@ __global__ void prompt_kernel(PromptArgs a) {
     }
 }
 
-template <typename T, int D>
+template <typename F, int D>
 hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
     constexpr int U = kRowsPerChunk;
-    constexpr int TPR = D / Traits<T>::EPT;
+    constexpr int TPR = D / F::EPT;
     const int G = waves * (64 / TPR);
     dim3 grid(a.lanes), block(64 * waves);
     switch (mode) {
         case MODE_SPARSE: {
             const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;
             if (U * G <= a.L_p + a.n_sink)
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
             else
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
             break;
         }
         case MODE_DENSE:
-            hipLaunchKernelGGL((decode_kernel<T, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<F, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
             break;
         case MODE_TOVA: {
             const size_t lds = (size_t)a.meta_stride * 4;
             if (U * G <= a.L_p)
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_TOVA, U, true>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_TOVA, U, true>), grid, block, lds, s, a);
             else
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_TOVA, U, false>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_TOVA, U, false>), grid, block, lds, s, a);
             break;
         }
         default: {  // MODE_H2O: slot metadata, then one fp64 logit per attended row
             const size_t lds = (size_t)a.meta_stride * 4 + (size_t)(a.L_p + a.N_cache) * 8;
             if (U * G <= a.L_p)
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_H2O, U, true>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_H2O, U, true>), grid, block, lds, s, a);
             else
-                hipLaunchKernelGGL((decode_kernel<T, D, MODE_H2O, U, false>), grid, block, lds, s, a);
+                hipLaunchKernelGGL((decode_kernel<F, D, MODE_H2O, U, false>), grid, block, lds, s, a);
             break;
         }
     }
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename F, int D>
 hipError_t launch_prompt_t(const PromptArgs& a, hipStream_t s) {
-    const long long chunks = (long long)a.B * a.H * a.L_p * 2 * (D / Traits<T>::EPT);
-    long long blocks = (chunks + 255) / 256;
+    const long long units =
+        (long long)a.B * a.H * a.L_p * 2 * (F::MX ? D / 32 : D * (int)sizeof(typename F::In) / 16);
+    long long blocks = (units + 255) / 256;
     const long long lane_blocks = ((long long)a.B * a.H + 255) / 256;
     if (blocks < lane_blocks) blocks = lane_blocks;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((prompt_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prompt_kernel<F, D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+template <typename F>
+hipError_t decode_for(int mode, int D, int waves, const DecodeArgs& a, hipStream_t s) {
+    return D == 128 ? launch_decode_t<F, 128>(mode, waves, a, s) : launch_decode_t<F, 64>(mode, waves, a, s);
+}
+
+template <typename F>
+hipError_t prompt_for(int D, const PromptArgs& a, hipStream_t s) {
+    return D == 128 ? launch_prompt_t<F, 128>(a, s) : launch_prompt_t<F, 64>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s) {
-    if (dtype == 1) {
-        if (D == 128) return launch_decode_t<uint16_t, 128>(mode, waves, a, s);
-        return launch_decode_t<uint16_t, 64>(mode, waves, a, s);
-    }
-    if (D == 128) return launch_decode_t<float, 128>(mode, waves, a, s);
-    return launch_decode_t<float, 64>(mode, waves, a, s);
+    if (dtype == 2) return decode_for<Mx8>(mode, D, waves, a, s);
+    if (dtype == 1) return decode_for<Plain<uint16_t>>(mode, D, waves, a, s);
+    return decode_for<Plain<float>>(mode, D, waves, a, s);
 }
 
 hipError_t launch_prompt(int dtype, int D, const PromptArgs& a, hipStream_t s) {
-    if (dtype == 1) {
-        if (D == 128) return launch_prompt_t<uint16_t, 128>(a, s);
-        return launch_prompt_t<uint16_t, 64>(a, s);
-    }
-    if (D == 128) return launch_prompt_t<float, 128>(a, s);
-    return launch_prompt_t<float, 64>(a, s);
+    if (dtype == 2) return prompt_for<Mx8>(D, a, s);
+    if (dtype == 1) return prompt_for<Plain<uint16_t>>(D, a, s);
+    return prompt_for<Plain<float>>(D, a, s);
 }
 
 }  // namespace dsa

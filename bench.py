@@ -69,6 +69,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
+    p.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 KV-cache leg")
     p.add_argument("--no-policies", action="store_true",
                    help="skip the baseline policies (SlidingWindow, StreamingLLM, TOVA, H2O) at equal N_att")
     p.add_argument("--summarize-trace", metavar="CSV",
@@ -83,14 +84,23 @@ def log(msg):
 
 
 # ----------------------------------------------------------------------------- byte model
+def row_bytes(w):
+    """Bytes of one cached K|V row: 2 d elements, or MXFP8 codes plus the 8-byte scale word."""
+    import synth
+
+    if w.dtype == synth.MXFP8:
+        return 2 * w.head_dim + 8
+    return 2 * w.head_dim * (2 if w.dtype == synth.BF16 else 4)
+
+
 def sparse_bytes_per_head_step(w, t):
     """Algorithmic HBM bytes of one lane at step t: the attended K|V rows (prompt,
     sinks, window; the current token's row comes from the appended input), the
     appended row written to the ring, q, the fp32 output and the index list."""
     import synth
 
-    es = 2 if w.dtype == synth.BF16 else 4
-    E = 2 * w.head_dim * es
+    es = 4 if w.dtype == synth.F32 else 2  # q (bf16 for an MXFP8 cache)
+    E = row_bytes(w)
     S = w.sink
     tw = t - S
     n_list = 0 if tw < 0 else min(tw + 1, w.N_att - S)
@@ -123,8 +133,8 @@ def policy_bytes_per_head_step(w, policy, t):
         return sparse_bytes_per_head_step(w.with_(sink=4 if policy == 1 else 0), t)
     if policy in (2, 3):
         return sparse_bytes_per_head_step(w.with_(N_r=w.N_att, sink=4 if policy == 3 else 0), t)
-    es = 2 if w.dtype == synth.BF16 else 4
-    E = 2 * w.head_dim * es
+    es = 4 if w.dtype == synth.F32 else 2
+    E = row_bytes(w)
     n = min(t + 1, w.N_att)
     n_meta = 4 + min(t, w.N_att)
     b = (w.L_p + n) * E + E + w.head_dim * es + 4 * w.head_dim + (n_meta + 3) // 4 * 16 + 8
@@ -136,8 +146,8 @@ def policy_bytes_per_head_step(w, policy, t):
 def dense_bytes_per_head_step(w, t):
     import synth
 
-    es = 2 if w.dtype == synth.BF16 else 4
-    E = 2 * w.head_dim * es
+    es = 4 if w.dtype == synth.F32 else 2
+    E = row_bytes(w)
     return (w.L_p + t + 1) * E + E + w.head_dim * es + 4 * w.head_dim
 
 
@@ -153,8 +163,8 @@ class Inputs:
 
         self.layers = []
         B, H, D, T, L = w.batch, w.heads, w.head_dim, w.L_dec, w.L_p
-        host_dt = torch.int16 if w.dtype == synth.BF16 else torch.float32
-        np_dt = np.uint16 if w.dtype == synth.BF16 else np.float32
+        host_dt = torch.int16 if w.input_dtype == synth.BF16 else torch.float32
+        np_dt = np.uint16 if w.input_dtype == synth.BF16 else np.float32
         pin = {}
         for name, shape in (("q", (T, B, H, D)), ("k", (T, B, H, D)), ("v", (T, B, H, D)),
                             ("kp", (B, L, H, D)), ("vp", (B, L, H, D))):
@@ -628,6 +638,18 @@ def main():
             log("policy %s: %.1f ms per decode, %.0f GB/s" % (POLICY_NAMES[policy], s_p * 1e3, b / s_p / 1e9))
             del m
         result["policies"] = pol
+
+    if not args.no_mxfp8 and w.dtype == synth.BF16:
+        wm = w.with_(dtype=synth.MXFP8)
+        m = SparseModel(wm, inputs, layers, dev, waves, streams=S)
+        s_m, _ = time_decodes(m, args.steps, args.warmup, dev)
+        b = sum(sparse_bytes_per_head_step(wm, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+        result["mxfp8_kv"] = {"value": head_steps / s_m, "unit": "head-steps/s", "ms_per_step": s_m * 1e3,
+                              "hbm_gbs": b / s_m / 1e9, "speedup_vs_bf16_kv": sec / s_m,
+                              "byte_ratio": total_bytes / b, "workspace_gb": m.nbytes * S * layers / 1e9,
+                              "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
+        log("mxfp8 kv: %.1f ms per decode, %.0f GB/s, %.2fx the bf16 cache" % (s_m * 1e3, b / s_m / 1e9, sec / s_m))
+        del m
 
     if args.sweep:
         sweep = []

@@ -17,7 +17,7 @@
  * Conventions
  *   - Lanes: lane = b * heads + h.  All lanes of a state share the step t.
  *   - Tensors passed per step are device pointers, row-major [batch][heads][head_dim]
- *     in the state's KV dtype (q, k, v) or fp32 (out).  The prompt is
+ *     in the state's KV dtype (q, k, v; bf16 for DSA_MXFP8) or fp32 (out).  The prompt is
  *     [batch][L_p][heads][head_dim].  Pointers must be 16-byte aligned.
  *   - Softmax scale is 1 / sqrt(head_dim); one softmax over prompt + selected
  *     decode rows; accumulation in fp32, the raw q.k logits in fp64.
@@ -61,7 +61,17 @@ typedef enum {
     DSA_E_NOMEM = -5      /* host allocation failed */
 } dsa_status;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+/*
+ * KV dtype of a state.  DSA_F32 / DSA_BF16: q, k, v and the cache in that
+ * type.  DSA_MXFP8: q, k, v and the prompt arrive in bf16 and the cache holds
+ * MXFP8 rows (OCP Microscaling v1.0: E4M3 elements, one E8M0 power-of-two
+ * scale per 32 elements, scale exponent floor(log2(max |v|)) - 8, elements
+ * rounded to nearest even and saturated at +-448); every decode row is
+ * attended in its quantised form, the current token's included.  The pages
+ * call KV quantization stackable with the selection (Section 6) and fix no
+ * format.  A row then takes 2 * head_dim + 8 bytes instead of 4 * head_dim.
+ */
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_MXFP8 = 2 } dsa_dtype;
 
 /* Largest N_att - sink the sparse kernel supports (its index list lives in LDS). */
 #define DSA_MAX_ATTEND 8192

@@ -228,14 +228,20 @@ def mxfp8_roundtrip(x):
 
 
 def lane_inputs(workload, layer, b, h, T=None):
-    """fp64 inputs of one lane from the shared seeded generator: (q, kp, vp, k, v)."""
+    """fp64 inputs of one lane from the shared seeded generator: (q, kp, vp, k, v).
+
+    For a workload with an MXFP8 cache the K / V rows come back as the cache
+    holds them (quantised and dequantised); q stays bf16."""
     import synth
 
     T = workload.L_dec if T is None else T
-    dt = workload.dtype
+    dt = workload.input_dtype
     q = widen(workload.lane(layer, b, h, synth.Q, 0, T), dt)
     k = widen(workload.lane(layer, b, h, synth.K, 0, T), dt)
     v = widen(workload.lane(layer, b, h, synth.V, 0, T), dt)
     kp = widen(workload.lane(layer, b, h, synth.KP), dt)
     vp = widen(workload.lane(layer, b, h, synth.VP), dt)
+    if workload.dtype == synth.MXFP8:
+        # an MXFP8 cache holds every K / V row (prompt and decode) quantised
+        k, v, kp, vp = (mxfp8_roundtrip(x) if x.size else x for x in (k, v, kp, vp))
     return q, kp, vp, k, v

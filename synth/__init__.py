@@ -21,6 +21,9 @@ _LIB = os.path.join(_HERE, "_libsynth.so")
 
 Q, K, V, KP, VP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
+# A workload whose KV cache is MXFP8: its inputs are generated in bf16 (the
+# quantisation belongs to the cache, not to the inputs).
+MXFP8 = 2
 
 
 def build() -> str:
@@ -99,6 +102,11 @@ class Workload:
     def lanes(self) -> int:
         return self.batch * self.heads
 
+    @property
+    def input_dtype(self) -> int:
+        """dtype of the generated q, k, v (MXFP8 caches take bf16 inputs)."""
+        return BF16 if self.dtype == MXFP8 else self.dtype
+
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
@@ -108,13 +116,13 @@ class Workload:
         ntok = self.L_dec - tok0 if ntok is None else ntok
         B, H, d = self.batch, self.heads, self.head_dim
         return fill(self.seed, stream, layer, d, self.grid_w, 0, B, 0, H, tok0, ntok,
-                    (ntok, B, H, d), (B * H * d, H * d, d), self.dtype, threads, out)
+                    (ntok, B, H, d), (B * H * d, H * d, d), self.input_dtype, threads, out)
 
     def prompt(self, layer, stream, threads=None, out=None):
         """Prompt K or V in the model layout ``[B][L_p][H][d]``."""
         B, H, d, L = self.batch, self.heads, self.head_dim, self.L_p
         return fill(self.seed, stream, layer, d, self.grid_w, 0, B, 0, H, 0, L,
-                    (B, L, H, d), (H * d, L * H * d, d), self.dtype, threads, out)
+                    (B, L, H, d), (H * d, L * H * d, d), self.input_dtype, threads, out)
 
     def lane(self, layer, b, h, stream, tok0=0, ntok=None, threads=None):
         """One (layer, batch, head) lane, ``[ntok][d]``; prompt streams give all L_p tokens."""
@@ -123,7 +131,7 @@ class Workload:
         ntok = self.L_dec - tok0 if ntok is None else ntok
         d = self.head_dim
         return fill(self.seed, stream, layer, d, self.grid_w, b, 1, h, 1, tok0, ntok,
-                    (ntok, d), (d, 0, 0), self.dtype, threads)
+                    (ntok, d), (d, 0, 0), self.input_dtype, threads)
 
 
 def n_att_for(L_dec: int, sparsity: float) -> int:

@@ -48,14 +48,16 @@ def _align(x):
     (8, 96, 4050, 810, 32, 128, 4, 1),
     (1, 16, 32, 8, 4, 64, 0, 0),
     (3, 0, 5, 5, 1, 64, 0, 1),
+    (96, 64, 288, 29, 32, 128, 0, 2),   # MXFP8 rows: 2 d codes + 8 scale bytes
+    (2, 16, 32, 8, 3, 64, 4, 2),
 ])
 def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
-    es = 2 if dt == 1 else 4
+    row = 2 * D + 8 if dt == 2 else 2 * D * (2 if dt == 1 else 4)
     lanes = B * H
     stride = (N_att - S + 7) // 8 * 8      # per-lane list padded to 16 bytes
-    want = _align(lanes * (L_p + N_r) * 2 * D * es) + _align(lanes * stride * 2)
+    want = _align(lanes * (L_p + N_r) * row) + _align(lanes * stride * 2)
     assert dsa.dsa_state_workspace_bytes(B, L_p, N_r, N_att, H, D, S, dt) == want
-    assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * 2 * D * es)
+    assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * row)
 
 
 @pytest.mark.parametrize("args", [
@@ -69,6 +71,7 @@ def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
     (1, 16, 32, 4, 4, 64, 4, 0),      # sink 4 needs N_att > 4
     (1, 16, 32, 8, 4, 64, 2, 0),      # sink must be 0 or 4
     (1, 16, 32, 8, 4, 64, 0, 7),      # dtype
+    (1, 16, 32, 8, 4, 64, 0, 3),      # dtype one past DSA_MXFP8
     (1, 16, 20000, 9000, 4, 64, 0, 1),  # list beyond LDS capacity
 ])
 def test_invalid_parameters_rejected(args):
