@@ -132,8 +132,9 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // group keeps at least the pipeline depth (4 rows) of work, and the workgroup
 // stays at 8 wavefronts or fewer (16 was slower at every measured shape).
 int choose_waves(const dsa_state* st, long long rows) {
-    if (st->waves) return st->waves;
-    const int ept = st->dtype == DSA_F32 ? 4 : 8;  // elements of K (and of V) per thread
+    const int max_w = st->dtype == DSA_MXFP8 ? 8 : 16;  // MXFP8 workgroups stop at 8 wavefronts
+    if (st->waves) return std::min(st->waves, max_w);
+    const int ept = st->dtype == DSA_F32 ? 4 : st->dtype == DSA_MXFP8 ? 16 : 8;  // elements per thread
     const int gpw = 64 / (st->D / ept);
     int w = 1;
     while (w < 8 && (long long)st->lanes * (2 * w) < 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;

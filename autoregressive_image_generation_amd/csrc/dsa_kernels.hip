@@ -8,8 +8,8 @@
 //
 // One workgroup per lane (one (sequence, head) of the layer), `waves` 64-wide
 // wavefronts.  Each thread group of TPR threads holds one cache row at a time,
-// 8 (bf16, MXFP8) or 4 (fp32) elements of K and of V per thread; a wavefront
-// works on 64 / TPR rows at a time.  Each group keeps its own online-softmax
+// 16 (MXFP8), 8 (bf16) or 4 (fp32) elements of K and of V per thread; a
+// wavefront works on 64 / TPR rows at a time.  Each group keeps its own online-softmax
 // state (m, l, acc) over the rows it visits; groups merge through DPP /
 // shuffles inside the wavefront and through LDS across wavefronts.
 // Single-query decode does about one flop per byte of KV, so the kernel is
@@ -28,8 +28,9 @@
 //     stackable with the selection): MXFP8 of the OCP Microscaling v1.0
 //     format.  K codes (D bytes, E4M3), V codes (D bytes), then an 8-byte
 //     scale word: byte b the E8M0 scale of K block b, byte 4 + b that of V
-//     block b, blocks of 32 elements.  A thread's chunk is 8 codes of K, 8 of
-//     V and the scale word.  q and the appended K/V arrive in bf16; the
+//     block b, blocks of 32 elements.  A thread's chunk is 16 codes of K, 16
+//     of V and the scale word (16-byte loads, as for the other formats: the
+//     per-row cost of the loop, not the bytes, bounds a row this short).  q and the appended K/V arrive in bf16; the
 //     appended row is quantised in the launch that appends it, and every
 //     decode row the attention reads, the current token's included, is the
 //     quantised one.
@@ -79,20 +80,20 @@ __device__ __forceinline__ void unpack(const uint4& x, float* f) {
 }
 
 // ---------------------------------------------------------------- MXFP8
-// E4M3 codes -> floats (gfx950 converts OCP E4M3 in hardware, exactly).
-__device__ __forceinline__ void unpack_e4m3(const uint2& c, float* f) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
-    const auto e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+// E4M3 codes -> floats (gfx950 converts OCP E4M3 in hardware, exactly); 4 codes per word.
+__device__ __forceinline__ void unpack_e4m3_word(uint32_t w, float* f) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
     f[0] = a[0];
     f[1] = a[1];
     f[2] = b[0];
     f[3] = b[1];
-    f[4] = d[0];
-    f[5] = d[1];
-    f[6] = e[0];
-    f[7] = e[1];
+}
+__device__ __forceinline__ void unpack_e4m3(const uint4& c, float* f) {
+    unpack_e4m3_word(c.x, f);
+    unpack_e4m3_word(c.y, f + 4);
+    unpack_e4m3_word(c.z, f + 8);
+    unpack_e4m3_word(c.w, f + 12);
 }
 
 // 2^(s - 127) of an E8M0 byte (s = 0 is 2^-127, a float subnormal).
@@ -142,13 +143,14 @@ struct Plain {
 struct Mx8 {
     using In = uint16_t;  // q and the appended rows arrive in bf16
     static constexpr bool MX = true;
-    static constexpr int EPT = 8;
+    static constexpr int EPT = 16;
     template <int D>
     static constexpr size_t row_bytes() {
         return (size_t)2 * D + 8;
     }
     struct Chunk {
-        uint2 k, v, s;
+        uint4 k, v;
+        uint2 s;
     };
 };
 
@@ -224,8 +226,10 @@ constexpr int kSelfOutOfStream = -2;
 // EARLY: every thread group's first U rows need no list or slot entry (U * G
 // <= number of prompt + sink rows), so they are requested before the lane's
 // index data has arrived.
+// MXFP8 holds 16 elements per thread and needs more than 128 VGPRs, so its
+// workgroups stop at 8 wavefronts.
 template <typename F, int D, int MODE, int U, bool EARLY>
-__global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a) {
     using T = typename F::In;
     constexpr bool MX = F::MX;
     constexpr int EPT = F::EPT;
@@ -285,7 +289,10 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         if (tid < nch) lc0 = load16(idx16 + tid);
         if (tid + (int)blockDim.x < nch) lc1 = load16(idx16 + tid + blockDim.x);
     }
-    const uint4 qx = load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT);
+    constexpr int QCH = EPT / IEPT > 0 ? EPT / IEPT : 1;  // 16-byte chunks of q per thread
+    uint4 qx[QCH];
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) qx[c] = load16(reinterpret_cast<const T*>(a.q) + (size_t)lane * D + sl * EPT + c * IEPT);
     uint4 ax = make_uint4(0, 0, 0, 0);
     if (tid < CH) ax = load16((tid < CH / 2 ? k_self : v_self) + (tid % (CH / 2)) * 16);
 
@@ -331,8 +338,8 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
         }
         if constexpr (MX) {
             d = self ? kSelfOutOfStream : d;  // the row address stays a valid cache row
-            kr = row + sl * 8;
-            vr = row + D + sl * 8;
+            kr = row + sl * 16;
+            vr = row + D + sl * 16;
             sr = row + 2 * D;
         } else {
             kr = (self ? k_self : row) + sl * 16;
@@ -343,8 +350,8 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     auto load_row = [&](const char* kr, const char* vr, const char* sr) {
         typename F::Chunk c;
         if constexpr (MX) {
-            c.k = load8_stream(kr);
-            c.v = load8_stream(vr);
+            c.k = load16_stream(kr);
+            c.v = load16_stream(vr);
             c.s = load8_stream(sr);
         } else {
             (void)sr;
@@ -389,7 +396,8 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     double qd[EPT];
     {
         float qf[EPT];
-        unpack<T>(qx, qf);
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) unpack<T>(qx[c], qf + c * IEPT);
 #pragma unroll
         for (int e = 0; e < EPT; ++e) qd[e] = (double)qf[e];
     }
@@ -424,9 +432,9 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
             // current token's placeholder): zero its bytes so that no NaN code
             // reaches the accumulator through a zero weight
             const uint32_t keep = valid ? 0xffffffffu : 0u;
-            unpack_e4m3(make_uint2(ch.k.x & keep, ch.k.y & keep), kf);
-            unpack_e4m3(make_uint2(ch.v.x & keep, ch.v.y & keep), vf);
-            const int b = sl >> 2;  // this thread's 8 elements lie in block b of 32
+            unpack_e4m3(make_uint4(ch.k.x & keep, ch.k.y & keep, ch.k.z & keep, ch.k.w & keep), kf);
+            unpack_e4m3(make_uint4(ch.v.x & keep, ch.v.y & keep, ch.v.z & keep, ch.v.w & keep), vf);
+            const int b = sl * EPT / 32;  // this thread's elements lie in block b of 32
             kscale = (double)e8m0_value((ch.s.x & keep) >> (8 * b) & 0xffu);
             vscale = e8m0_value((ch.s.y & keep) >> (8 * b) & 0xffu);
         } else {
@@ -554,16 +562,23 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
     if (wave != 0) return;
 
     // MXFP8: the current token's row, quantised above, enters after the merge
-    // of all other rows, in the lanes of wave 0's first group (its K half is
-    // in lanes 0 .. TPR-1, its V half in lanes TPR .. 2 TPR-1; CH = 2 TPR).
+    // of all other rows, in the lanes of wave 0's first group.  Lane c < CH/2
+    // holds K codes 8c .. 8c+7 and lane CH/2 + c the same V codes, so group
+    // lane sl gathers chunks 2 sl and 2 sl + 1 of each half.
     bool self_in = false;
     int self_j = -1;
     double self_s = 0.0;
     float self_vf[EPT];
     float self_vs = 1.0f;
     if constexpr (MX) {
-        const uint2 vcode = make_uint2(__shfl((int)qcode.x, wl + TPR), __shfl((int)qcode.y, wl + TPR));
-        self_vs = e8m0_value((uint32_t)__shfl((int)qscale, wl + TPR));
+        static_assert(EPT == 16, "two 8-code chunks per thread");
+        const int k0l = 2 * wl, v0l = CH / 2 + 2 * wl;  // source lanes (only lanes < TPR use them)
+        const uint4 kcode = make_uint4(__shfl((int)qcode.x, k0l), __shfl((int)qcode.y, k0l),
+                                       __shfl((int)qcode.x, k0l + 1), __shfl((int)qcode.y, k0l + 1));
+        const uint4 vcode = make_uint4(__shfl((int)qcode.x, v0l), __shfl((int)qcode.y, v0l),
+                                       __shfl((int)qcode.x, v0l + 1), __shfl((int)qcode.y, v0l + 1));
+        const float self_ks = e8m0_value((uint32_t)__shfl((int)qscale, k0l));
+        self_vs = e8m0_value((uint32_t)__shfl((int)qscale, v0l));
         if constexpr (MODE == MODE_SPARSE) {
             self_j = s_self_j;
             self_in = self_j >= 0;
@@ -572,12 +587,12 @@ __global__ void __launch_bounds__(1024) decode_kernel(DecodeArgs a) {
             self_j = MODE == MODE_TOVA ? fslot : -1;
         }
         float kf[EPT];
-        unpack_e4m3(qcode, kf);
+        unpack_e4m3(kcode, kf);
         unpack_e4m3(vcode, self_vf);
         double part = 0.0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
-        self_s = group_sum<TPR>(part * (double)e8m0_value(qscale));
+        self_s = group_sum<TPR>(part * (double)self_ks);
     }
 
     if (wl < TPR) {

@@ -35,9 +35,12 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC = {
     # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
     # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "94aec6bd99f46058"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "kernel_sha256_16": "0b36e8ec01d50440"},
     # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.5e6, "kernel_sha256_16": "94aec6bd99f46058"},
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.5e6, "kernel_sha256_16": "0b36e8ec01d50440"},
+    # MXFP8 cache, two micro-batches of 48: dispatches 24000-24599 of its own decode kernel
+    # (steps 400-409), algorithmic 39.39 MB; its 264-byte rows straddle 64-byte segments
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.98e6, "kernel_sha256_16": "0b36e8ec01d50440"},
 }
 
 
@@ -646,6 +649,8 @@ def main():
         b = sum(sparse_bytes_per_head_step(wm, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
         result["mxfp8_kv"] = {"value": head_steps / s_m, "unit": "head-steps/s", "ms_per_step": s_m * 1e3,
                               "hbm_gbs": b / s_m / 1e9, "speedup_vs_bf16_kv": sec / s_m,
+                              "traffic_per_launch": traffic_for(w.name + "_mxfp8", S),
+                              "algorithmic_bytes_per_launch": b / (w.L_dec * layers * S),
                               "byte_ratio": total_bytes / b, "workspace_gb": m.nbytes * S * layers / 1e9,
                               "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
         log("mxfp8 kv: %.1f ms per decode, %.0f GB/s, %.2fx the bf16 cache" % (s_m * 1e3, b / s_m / 1e9, sec / s_m))

@@ -224,8 +224,9 @@ int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, co
 
 /*
  * Workgroup size of the decode kernels, in 64-wide wavefronts per lane:
- * 1, 2, 4, 8 or 16, or 0 for the library's choice.  Results do not depend on
- * it except for fp32 rounding order in the softmax sums.
+ * 1, 2, 4, 8 or 16, or 0 for the library's choice (DSA_MXFP8 states use at
+ * most 8).  Results do not depend on it except for fp32 rounding order in
+ * the softmax sums.
  */
 int dsa_set_waves(dsa_state* st, int waves_per_lane);
 
