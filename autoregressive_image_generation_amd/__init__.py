@@ -27,10 +27,12 @@ from .binding import (
     dsa_append_decode_step,
     dsa_append_kv,
     dsa_append_prompt,
+    dsa_attention_profile,
     dsa_decode_step,
     dsa_last_error,
     dsa_policy_state_init,
     dsa_policy_workspace_bytes,
+    dsa_profile_workspace_bytes,
     dsa_read_state,
     dsa_set_stream,
     dsa_set_waves,

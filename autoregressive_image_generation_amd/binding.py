@@ -39,6 +39,8 @@ _SIGNATURES = {
     "dense_append_kv": (_c_int, [_P, _P, _P]),
     "dense_decode_step": (_c_int, [_P, _P, _P]),
     "dense_append_decode_step": (_c_int, [_P, _P, _P, _P, _P]),
+    "dsa_profile_workspace_bytes": (_c_size, [_c_int] * 4),
+    "dsa_attention_profile": (_c_int, [_P, _P, _P] + [_c_int] * 7 + [_P, _c_size, _P, _P, _P, _P]),
     "dsa_set_waves": (_c_int, [_P, _c_int]),
     "dsa_state_step": (_c_int, [_P]),
     "dsa_state_destroy": (_c_int, [_P]),
@@ -212,6 +214,17 @@ def dense_decode_step(st, q_t, out):
 
 def dense_append_decode_step(st, k_t, v_t, q_t, out):
     return _check(library().dense_append_decode_step(st, _ptr(k_t), _ptr(v_t), _ptr(q_t), _ptr(out)))
+
+
+def dsa_profile_workspace_bytes(batch, heads, L_p, T) -> int:
+    return int(library().dsa_profile_workspace_bytes(batch, heads, L_p, T))
+
+
+def dsa_attention_profile(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, workspace, workspace_bytes,
+                          mass, vert, diag, stream=None):
+    return _check(library().dsa_attention_profile(_ptr(q), _ptr(k), _ptr(k_p), batch, heads, head_dim, L_p, T, dtype,
+                                                  max_dist, _ptr(workspace), workspace_bytes, _ptr(mass), _ptr(vert),
+                                                  _ptr(diag), _stream(stream)))
 
 
 def dsa_set_waves(st, waves_per_lane):

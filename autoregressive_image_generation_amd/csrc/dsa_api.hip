@@ -577,6 +577,52 @@ int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, co
     return rc;
 }
 
+size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T) {
+    if (batch < 1 || heads < 1 || L_p < 0 || T < 2) return 0;
+    const size_t lanes = (size_t)batch * heads;
+    return align_up(lanes * (size_t)T * (size_t)T * sizeof(float)) + align_up(lanes * (size_t)T * 3 * sizeof(float));
+}
+
+int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
+                          int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
+                          double* vert, double* diag, void* hip_stream) {
+    int rc = check_common(batch, L_p, heads, head_dim, dtype);
+    if (rc) return rc;
+    if (dtype == DSA_MXFP8) return fail(DSA_E_INVAL, "the profile takes fp32 or bf16 inputs");
+    if (T < 2) return fail(DSA_E_INVAL, "T must be >= 2 (got %d)", T);
+    if (max_dist < 1 || max_dist > T - 1) return fail(DSA_E_INVAL, "max_dist must be in [1, T - 1] (got %d)", max_dist);
+    const long long lanes = (long long)batch * heads;
+    if (lanes * ((T + 15) / 16) > 0x7fffffffll || (lanes + 7) / 8 * 8 * (long long)max_dist > 0x7fffffffll)
+        return fail(DSA_E_INVAL, "grid too large");
+    if (!q || !k || (L_p > 0 && !k_p)) return fail(DSA_E_INVAL, "q / k / k_p is NULL");
+    if (!aligned16(q) || !aligned16(k) || (L_p > 0 && !aligned16(k_p)))
+        return fail(DSA_E_INVAL, "q / k / k_p must be 16-byte aligned");
+    if (!mass || !vert || !diag) return fail(DSA_E_INVAL, "an output pointer is NULL");
+    if (((uintptr_t)mass | (uintptr_t)vert | (uintptr_t)diag) & 7u)
+        return fail(DSA_E_INVAL, "outputs must be 8-byte aligned");
+    rc = check_workspace(d_workspace, workspace_bytes, dsa_profile_workspace_bytes(batch, heads, L_p, T));
+    if (rc) return rc;
+    dsa::ProfileArgs a;
+    a.q = q;
+    a.k = k;
+    a.k_p = k_p;
+    a.P = static_cast<float*>(d_workspace);
+    a.mass_rows = reinterpret_cast<float*>(static_cast<char*>(d_workspace) +
+                                           align_up((size_t)lanes * (size_t)T * (size_t)T * sizeof(float)));
+    a.mass = mass;
+    a.vert = vert;
+    a.diag = diag;
+    a.lanes = (int)lanes;
+    a.B = batch;
+    a.H = heads;
+    a.L_p = L_p;
+    a.T = T;
+    a.max_dist = max_dist;
+    hipError_t e = dsa::launch_profile(dtype, head_dim, a, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "profile launch");
+    return DSA_OK;
+}
+
 int dsa_set_waves(dsa_state* st, int waves_per_lane) {
     int rc = check_state(st, 0);
     if (rc) return rc;

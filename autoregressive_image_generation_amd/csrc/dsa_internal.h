@@ -69,7 +69,21 @@ struct PromptArgs {
     int B, H, L_p, list_stride;
 };
 
+// Attention-map characterization (dsa_profile.hip).
+struct ProfileArgs {
+    const void* q;         // [T][B][H][D] decode queries
+    const void* k;         // [T][B][H][D] decode keys
+    const void* k_p;       // [B][L_p][H][D] prompt keys
+    float* P;              // workspace: [lanes][T][T] decode probabilities (j <= i written)
+    float* mass_rows;      // workspace: [lanes][T][3] prompt / local / middle mass per query
+    double* mass;          // out: [lanes][3] mean over queries
+    double* vert;          // out: [lanes][max_dist] mean vertical cosine similarity, distance 1..max_dist
+    double* diag;          // out: [lanes][max_dist] mean diagonal cosine similarity
+    int lanes, B, H, L_p, T, max_dist;
+};
+
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_profile(int dtype, int D, const ProfileArgs& a, hipStream_t s);
 hipError_t launch_prompt(int dtype, int D, const PromptArgs& a, hipStream_t s);
 
 }  // namespace dsa

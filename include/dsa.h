@@ -230,6 +230,32 @@ int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, co
  */
 int dsa_set_waves(dsa_state* st, int waves_per_lane);
 
+/*
+ * Attention-map characterization (Section 3.4 of the pages: Fig. 8, attention
+ * mass on prompt / local / middle tokens; Fig. 10, vertical vs diagonal
+ * cosine similarity of attention score vectors), on the dense decode map of
+ * T decode steps: query t attends the prompt and decode positions 0..t, one
+ * softmax with scale 1 / sqrt(head_dim).  Per lane (b * heads + h):
+ *   mass [lanes][3]  - mean over queries of the mass on the prompt, on the
+ *                      local tokens (the ceil((t + 1) / 10) most recent
+ *                      decoded tokens, the current one included) and on the
+ *                      other decoded tokens;
+ *   vert, diag [lanes][max_dist] - for d = 1..max_dist, the mean over
+ *                      i in [0, T - d) of cos(P[i][0..i], P[i+d][0..i]) and
+ *                      of cos(P[i][0..i], P[i+d][d..i+d]), P the decode
+ *                      probabilities (prompt columns left out).
+ * q, k: [T][batch][heads][head_dim], k_p: [batch][L_p][heads][head_dim], in
+ * dtype DSA_F32 or DSA_BF16, 16-byte aligned.  Outputs: device fp64 arrays,
+ * 8-byte aligned.  1 <= max_dist <= T - 1.  The workspace (size from
+ * dsa_profile_workspace_bytes, 256-byte aligned) holds the fp32 map
+ * [lanes][T][T] and per-query mass; it is the caller's.  Asynchronous on
+ * hip_stream (NULL = null stream).  The logits are MFMA tiles (fp32 sums).
+ */
+size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T);
+int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
+                          int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
+                          double* vert, double* diag, void* hip_stream);
+
 /* Next step index of a sparse or dense state (or a negative dsa_status). */
 int dsa_state_step(const dsa_state* st);
 

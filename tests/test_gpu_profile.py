@@ -1,0 +1,133 @@
+"""GPU parity of the attention-map characterization (Section 3.4, Figs. 8 and 10)
+against the fp64 oracle in oracle/charmap.py.
+
+Tolerance: 1e-4 absolute on the mass fractions and the mean cosines.  Both
+sides see the same inputs; the GPU sums the logits in fp32 (MFMA) and takes
+fp32 exponentials, which moves a probability by ~1e-6 relative.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_image_generation_amd as dsa
+import oracle
+import synth
+from gpu_util import device_inputs, to_dev
+from oracle import charmap
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_profile(q, k, kp, B, H, D, L_p, T, dtype, max_dist):
+    lanes = B * H
+    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L_p, T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    mass = torch.empty((lanes, 3), dtype=torch.float64, device=DEV)
+    vert = torch.empty((lanes, max_dist), dtype=torch.float64, device=DEV)
+    diag = torch.empty((lanes, max_dist), dtype=torch.float64, device=DEV)
+    dsa.dsa_attention_profile(q, k, kp if L_p else None, B, H, D, L_p, T, dtype, max_dist, ws, nbytes, mass, vert,
+                              diag, torch.cuda.current_stream(DEV))
+    torch.cuda.synchronize(DEV)
+    return mass.cpu().numpy(), vert.cpu().numpy(), diag.cpu().numpy()
+
+
+def check_workload(w, max_dist, lanes=None, layer=0):
+    T = w.L_dec
+    say("profile %s T=%d L_p=%d d=%d max_dist=%d" % (w.name, T, w.L_p, w.head_dim, max_dist))
+    q, k, v, kp, vp = device_inputs(w, layer, T, DEV)
+    mass, vert, diag = run_profile(q, k, kp, w.batch, w.heads, w.head_dim, w.L_p, T, w.dtype, max_dist)
+    lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    worst = 0.0
+    for (b, h) in lanes:
+        lq, lkp, lvp, lk, lv = oracle.lane_inputs(w, layer, b, h, T)
+        rm, rv, rd = charmap.profile_lane(lq, lkp, lk, max_dist)
+        lane = b * w.heads + h
+        err = max(np.abs(mass[lane] - rm).max(), np.abs(vert[lane] - rv).max(), np.abs(diag[lane] - rd).max())
+        worst = max(worst, err)
+        assert err <= TOL, (b, h, err)
+    say("  lanes=%d max_err=%.3g" % (len(lanes), worst))
+    return mass, vert, diag
+
+
+def tiny(**kw):
+    return synth.WORKLOADS["tiny_fp32"].with_(**kw)
+
+
+def test_tiny_fp32_every_lane():
+    check_workload(tiny(), 20)
+
+
+@pytest.mark.parametrize("dt,D", [(synth.BF16, 64), (synth.BF16, 128), (synth.F32, 128)])
+def test_dtypes_and_head_dims(dt, D):
+    check_workload(tiny(dtype=dt, head_dim=D, batch=3, heads=5, L_p=5), 12)
+
+
+@pytest.mark.parametrize("kw,max_dist", [(dict(L_p=0), 8), (dict(L_dec=37), 36), (dict(L_dec=2, L_p=3), 1),
+                                          (dict(batch=9, heads=1), 4)])
+def test_edge_cases(kw, max_dist):
+    check_workload(tiny(**kw), max_dist)
+
+
+def _as_inputs(q, kp, k, D):
+    """fp32 lane arrays -> device tensors in the library layouts (one lane)."""
+    T, d = q.shape
+
+    def pad(x):
+        y = np.zeros((x.shape[0], D), np.float32)
+        y[:, :d] = x
+        return y
+
+    return (to_dev(pad(q)[:, None, None, :], DEV), to_dev(pad(k)[:, None, None, :], DEV),
+            to_dev(pad(kp)[None, :, None, :], DEV))
+
+
+def test_relative_position_attention_is_diagonal_on_gpu():
+    from test_oracle_charmap import rotary_relative
+
+    T, L_p = 48, 6
+    q, kp, k = rotary_relative(T, L_p, 0.4, 2)
+    # zero-padded to head_dim 64 on both sides (the softmax scale is 1 / sqrt(64))
+    q, kp, k = (np.pad(x.astype(np.float32).astype(np.float64), ((0, 0), (0, 64 - x.shape[1]))) for x in (q, kp, k))
+    dq, dk, dkp = _as_inputs(q, kp, k, 64)
+    mass, vert, diag = run_profile(dq, dk, dkp, 1, 1, 64, L_p, T, synth.F32, 10)
+    np.testing.assert_allclose(diag[0], 1.0, atol=1e-5)
+    rm, rv, rd = charmap.profile_lane(q, kp, k, 10)
+    np.testing.assert_allclose(vert[0], rv, atol=TOL)
+    np.testing.assert_allclose(mass[0], rm, atol=TOL)
+
+
+def test_uniform_attention_on_gpu():
+    T, L_p, d = 40, 7, 64
+    rng = np.random.default_rng(1)
+    q, kp, k = np.zeros((T, d)), rng.normal(size=(L_p, d)), rng.normal(size=(T, d))
+    dq, dk, dkp = _as_inputs(q, kp, k, d)
+    mass, vert, diag = run_profile(dq, dk, dkp, 1, 1, d, L_p, T, synth.F32, 6)
+    want = np.zeros(3)
+    for t in range(T):
+        n = L_p + t + 1
+        loc = math.ceil((t + 1) / 10)
+        want += (L_p / n, loc / n, (t + 1 - loc) / n)
+    np.testing.assert_allclose(mass[0], want / T, atol=1e-6)
+    np.testing.assert_allclose(vert[0], 1.0, atol=1e-6)
+    np.testing.assert_allclose(diag[0], 1.0, atol=1e-6)
+
+
+def test_janus_pro_7b_shape_one_layer_sampled_lanes():
+    w = synth.WORKLOADS["janus_pro_7b"]
+    rng = np.random.default_rng(9)
+    lanes = sorted({(0, 0), (w.batch - 1, w.heads - 1)} | {(int(rng.integers(w.batch)), int(rng.integers(w.heads)))
+                                                           for _ in range(2)})
+    mass, vert, diag = check_workload(w, 48, lanes=lanes, layer=w.layers - 1)
+    # every lane (not only the sample): fractions sum to 1, cosines in (0, 1]
+    np.testing.assert_allclose(mass.sum(axis=1), 1.0, atol=1e-5)
+    assert ((vert > 0) & (vert <= 1 + 1e-6)).all() and ((diag > 0) & (diag <= 1 + 1e-6)).all()
