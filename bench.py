@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
     p.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 KV-cache leg")
+    p.add_argument("--profile-dist", type=int, default=48,
+                   help="attention-map characterization of layer 0 up to this query distance (0: skip)")
     p.add_argument("--no-policies", action="store_true",
                    help="skip the baseline policies (SlidingWindow, StreamingLLM, TOVA, H2O) at equal N_att")
     p.add_argument("--summarize-trace", metavar="CSV",
@@ -419,6 +421,56 @@ def kernel_durations(model, layers, dev):
     return per_step
 
 
+def characterize(w, inputs, dev, max_dist, reps=3):
+    """Section 3.4 measurements (Figs. 8 and 10) on the dense decode map of
+    layer 0, all lanes: mean mass split and vertical / diagonal similarity,
+    with the time of the two kernels (HIP events on the launch stream)."""
+    import numpy as np
+    import torch
+
+    import autoregressive_image_generation_amd as dsa
+
+    x = inputs.layers[0]
+    B, H, D, L, T = w.batch, w.heads, w.head_dim, w.L_p, w.L_dec
+    lanes = B * H
+    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L, T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    mass = torch.empty((lanes, 3), dtype=torch.float64, device=dev)
+    vert = torch.empty((lanes, max_dist), dtype=torch.float64, device=dev)
+    diag = torch.empty((lanes, max_dist), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        dsa.dsa_attention_profile(x["q"], x["k"], x["kp"] if L else None, B, H, D, L, T, w.input_dtype, max_dist, ws,
+                                  nbytes, mass, vert, diag, stream)
+
+    call()
+    torch.cuda.synchronize(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(stop) / reps
+    m = mass.cpu().numpy().mean(axis=0)
+    v = vert.cpu().numpy().mean(axis=0)
+    g = diag.cpu().numpy().mean(axis=0)
+    # algorithmic work of the map: one q.k per (query, causal key), the decode probabilities written once
+    keys = T * L + T * (T + 1) // 2
+    flops = 2.0 * D * keys * lanes
+    map_bytes = 4.0 * (T * (T + 1) // 2) * lanes
+    picks = sorted({1, 2, w.grid_w, 2 * w.grid_w, max_dist} & set(range(1, max_dist + 1)))
+    log("characterization: %.2f ms; mass prompt/local/middle %.3f/%.3f/%.3f" % (ms, *m))
+    return {"layer": 0, "lanes": lanes, "T": T, "max_dist": max_dist, "ms": ms,
+            "mass_prompt_local_middle": [float(a) for a in m],
+            "vertical": {str(d): float(v[d - 1]) for d in picks},
+            "diagonal": {str(d): float(g[d - 1]) for d in picks},
+            "diagonal_minus_vertical_mean": float((g - v).mean()),
+            "map_flop": flops, "map_prob_bytes": map_bytes,
+            "note": "ms covers both kernels (map: MFMA logits + softmax, writes the fp32 map; similarity)"}
+
+
 def cpu_baseline(w, target_cpu_seconds):
     """The oracle as it stands on a bounded, seeded sample of lanes (all L_dec
     steps each), one lane per host thread; returns the JSON object.  Inputs are
@@ -655,6 +707,9 @@ def main():
                               "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
         log("mxfp8 kv: %.1f ms per decode, %.0f GB/s, %.2fx the bf16 cache" % (s_m * 1e3, b / s_m / 1e9, sec / s_m))
         del m
+
+    if args.profile_dist > 0:
+        result["characterization"] = characterize(w, inputs, dev, args.profile_dist)
 
     if args.sweep:
         sweep = []

@@ -233,6 +233,38 @@ def test_full_size_workload_sampled_lanes(name):
     assert ok.all()
 
 
+@pytest.mark.parametrize("name", ["janus_pro_1b", "janus_pro_7b"])
+def test_full_size_every_lane_of_one_layer(name):
+    """Every lane of one full layer (512 / 3072 lanes x 576 steps) in the
+    benchmarked launch shape against the oracle: exact choice and eviction
+    traces, outputs within the bf16 bound (lockstep per lane, in a thread pool)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w = synth.WORKLOADS[name]
+    layer = 0
+    T = w.L_dec
+    say("every lane: %s layer %d (%d lanes)" % (name, layer, w.lanes))
+    ins = device_inputs(w, layer, T, DEV)
+    out, trace, _ = run_sparse(w, ins, T, DEV)
+    host = {n: x.cpu().numpy().view(np.uint16) for n, x in zip(("q", "k", "v", "kp", "vp"), ins)}
+    out = out.cpu().numpy()
+
+    def one(lane):
+        b, h = divmod(lane, w.heads)
+        li = tuple(oracle.widen(a, w.dtype) for a in (host["q"][:, b, h], host["kp"][b, :, h], host["vp"][b, :, h],
+                                                     host["k"][:, b, h], host["v"][:, b, h]))
+        st = {}
+        check_lane(w, li, out[:, b, h, :], trace[:, b, h, :], st)
+        return st
+
+    with ThreadPoolExecutor(16) as ex:
+        stats = list(ex.map(one, range(w.lanes)))
+    sel = sum(s["selections"] for s in stats)
+    ties = sum(s["near_ties"] for s in stats)
+    err = max(s["max_err"] for s in stats)
+    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g" % (w.lanes, sel, ties, err))
+
+
 def test_dense_full_size_janus7b_batch32_sampled():
     w = synth.WORKLOADS["janus_pro_7b"].with_(batch=32)
     T = w.L_dec
