@@ -39,7 +39,7 @@ _SIGNATURES = {
     "dense_append_kv": (_c_int, [_P, _P, _P]),
     "dense_decode_step": (_c_int, [_P, _P, _P]),
     "dense_append_decode_step": (_c_int, [_P, _P, _P, _P, _P]),
-    "dsa_profile_workspace_bytes": (_c_size, [_c_int] * 4),
+    "dsa_profile_workspace_bytes": (_c_size, [_c_int] * 5),
     "dsa_attention_profile": (_c_int, [_P, _P, _P] + [_c_int] * 7 + [_P, _c_size, _P, _P, _P, _P]),
     "dsa_set_waves": (_c_int, [_P, _c_int]),
     "dsa_state_step": (_c_int, [_P]),
@@ -216,8 +216,8 @@ def dense_append_decode_step(st, k_t, v_t, q_t, out):
     return _check(library().dense_append_decode_step(st, _ptr(k_t), _ptr(v_t), _ptr(q_t), _ptr(out)))
 
 
-def dsa_profile_workspace_bytes(batch, heads, L_p, T) -> int:
-    return int(library().dsa_profile_workspace_bytes(batch, heads, L_p, T))
+def dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist) -> int:
+    return int(library().dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist))
 
 
 def dsa_attention_profile(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, workspace, workspace_bytes,

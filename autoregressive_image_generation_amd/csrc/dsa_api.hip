@@ -577,10 +577,18 @@ int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, co
     return rc;
 }
 
-size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T) {
-    if (batch < 1 || heads < 1 || L_p < 0 || T < 2) return 0;
+static size_t profile_map_bytes(size_t lanes, int T) { return align_up(lanes * (size_t)T * (size_t)T * sizeof(float)); }
+static size_t profile_mass_bytes(size_t lanes, int T) { return align_up(lanes * (size_t)T * 3 * sizeof(float)); }
+
+// Workspace of a profile: the fp32 map [lanes][T][T], the per-query mass
+// [lanes][T][3] and the per-row-tile cosine sums [lanes][ceil(T/16)][2 max_dist].
+size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T, int max_dist) {
+    if (batch < 1 || heads < 1 || L_p < 0 || T < 2 || max_dist < 1 || max_dist > T - 1 ||
+        max_dist > dsa::kMaxProfileDist)
+        return 0;
     const size_t lanes = (size_t)batch * heads;
-    return align_up(lanes * (size_t)T * (size_t)T * sizeof(float)) + align_up(lanes * (size_t)T * 3 * sizeof(float));
+    return profile_map_bytes(lanes, T) + profile_mass_bytes(lanes, T) +
+           align_up(lanes * (size_t)((T + 15) / 16) * 2 * (size_t)max_dist * sizeof(double));
 }
 
 int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
@@ -590,25 +598,26 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
     if (rc) return rc;
     if (dtype == DSA_MXFP8) return fail(DSA_E_INVAL, "the profile takes fp32 or bf16 inputs");
     if (T < 2) return fail(DSA_E_INVAL, "T must be >= 2 (got %d)", T);
-    if (max_dist < 1 || max_dist > T - 1) return fail(DSA_E_INVAL, "max_dist must be in [1, T - 1] (got %d)", max_dist);
+    if (max_dist < 1 || max_dist > T - 1 || max_dist > dsa::kMaxProfileDist)
+        return fail(DSA_E_INVAL, "max_dist must be in [1, min(T - 1, %d)] (got %d)", dsa::kMaxProfileDist, max_dist);
     const long long lanes = (long long)batch * heads;
-    if (lanes * ((T + 15) / 16) > 0x7fffffffll || (lanes + 7) / 8 * 8 * (long long)max_dist > 0x7fffffffll)
-        return fail(DSA_E_INVAL, "grid too large");
+    if ((lanes + 7) / 8 * 8 * ((T + 15) / 16) > 0x7fffffffll) return fail(DSA_E_INVAL, "grid too large");
     if (!q || !k || (L_p > 0 && !k_p)) return fail(DSA_E_INVAL, "q / k / k_p is NULL");
     if (!aligned16(q) || !aligned16(k) || (L_p > 0 && !aligned16(k_p)))
         return fail(DSA_E_INVAL, "q / k / k_p must be 16-byte aligned");
     if (!mass || !vert || !diag) return fail(DSA_E_INVAL, "an output pointer is NULL");
     if (((uintptr_t)mass | (uintptr_t)vert | (uintptr_t)diag) & 7u)
         return fail(DSA_E_INVAL, "outputs must be 8-byte aligned");
-    rc = check_workspace(d_workspace, workspace_bytes, dsa_profile_workspace_bytes(batch, heads, L_p, T));
+    rc = check_workspace(d_workspace, workspace_bytes, dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist));
     if (rc) return rc;
     dsa::ProfileArgs a;
     a.q = q;
     a.k = k;
     a.k_p = k_p;
     a.P = static_cast<float*>(d_workspace);
-    a.mass_rows = reinterpret_cast<float*>(static_cast<char*>(d_workspace) +
-                                           align_up((size_t)lanes * (size_t)T * (size_t)T * sizeof(float)));
+    a.mass_rows = reinterpret_cast<float*>(static_cast<char*>(d_workspace) + profile_map_bytes(lanes, T));
+    a.partial = reinterpret_cast<double*>(static_cast<char*>(d_workspace) + profile_map_bytes(lanes, T) +
+                                          profile_mass_bytes(lanes, T));
     a.mass = mass;
     a.vert = vert;
     a.diag = diag;

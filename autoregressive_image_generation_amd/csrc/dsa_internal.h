@@ -79,8 +79,10 @@ struct ProfileArgs {
     double* mass;          // out: [lanes][3] mean over queries
     double* vert;          // out: [lanes][max_dist] mean vertical cosine similarity, distance 1..max_dist
     double* diag;          // out: [lanes][max_dist] mean diagonal cosine similarity
+    double* partial;       // workspace: [lanes][row tiles][max_dist][2] per-tile cosine sums
     int lanes, B, H, L_p, T, max_dist;
 };
+constexpr int kMaxProfileDist = 256;  // per-distance sums of a row tile live in LDS
 
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_profile(int dtype, int D, const ProfileArgs& a, hipStream_t s);

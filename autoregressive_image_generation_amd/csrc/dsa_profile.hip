@@ -4,19 +4,31 @@
 // workload (Fig. 8: attention mass on prompt / local / middle tokens; Fig. 10:
 // vertical vs diagonal cosine similarity of attention score vectors).
 //
-// profile_map_kernel: one wavefront per (lane, 16 queries).  The logits
-// Q K^T are a dense contraction, computed in 16 x 16 tiles with MFMA (bf16:
-// v_mfma_f32_16x16x16_bf16, fp32: v_mfma_f32_16x16x4_f32; fp32 accumulation).
-// Pass 1 keeps an online (max, sum) per query over the key tiles, pass 2
-// recomputes the tiles, writes the decode probabilities P[i][j] (j <= i) and
-// the per-query mass split.  No LDS holds a whole row, so T is not limited
-// by LDS.
+// profile_map_kernel: one wavefront per (lane, 16 queries), four per
+// workgroup sharing each 16-key tile through LDS.  The logits Q K^T are a
+// dense contraction, computed in 16 x 16 tiles with MFMA (bf16:
+// v_mfma_f32_16x16x16_bf16, fp32: v_mfma_f32_16x16x4_f32; fp32 sums), the
+// query operand held in registers.  Pass 1 keeps each lane's online
+// (max, sum) over its key columns and merges the 16 lanes of a query once;
+// pass 2 recomputes the tiles, writes the decode probabilities P[i][j]
+// (j <= i) and the per-query mass split.
 //
-// profile_sim_kernel: one workgroup per (lane, query distance d); its
-// wavefronts take queries i in turn and reduce the five dot products of
-// rows i and i + d (P[i][0..i] against P[i+d][0..i] and P[i+d][d..i+d]).
-// Workgroups go to the 8 XCDs round-robin, so the grid is ordered to give all
-// distances of a lane the same XCD: they reread the lane's map from one L2.
+// profile_gram_kernel: every similarity term is a band of a Gram matrix.
+// With Q[i][o] = P[i][i - o] (the map in offset coordinates: o = i - j),
+//   vertical dot   sum_j P[i][j] P[i+d][j]        = (P P^T)[i][i+d]
+//   diagonal dot   sum_j P[i][j] P[i+d][j+d]      = (Q Q^T)[i][i+d]
+//   |P[i+d][0..i]|^2                             = (L (P.P)^T)[i][i+d]
+//   |P[i+d][d..i+d]|^2                           = (L (Q.Q)^T)[i][i+d]
+//   |P[i][0..i]|^2                               = (P P^T)[i][i]
+// with L[i][k] = 1 for k <= i (P[i][k] = 0 beyond k = i).  A workgroup of
+// four wavefronts takes 64 rows; each wavefront computes the 16 x 16 tiles
+// of the four products for its 16 rows and the columns i + 1 .. i +
+// max_dist with MFMA (v_mfma_f32_16x16x4_f32), four column tiles per pass,
+// from 32-column chunks of the rows staged once for all four wavefronts in
+// LDS (padded stride: no bank conflicts), and adds each cosine into
+// per-distance sums.
+// profile_reduce_kernel: per lane, the sums over row tiles in order, the
+// means, and the mean mass split.
 #include <math.h>
 #include <stdint.h>
 
@@ -28,62 +40,95 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
-// 16 x 16 logit tile S[r][c] = q_{i0+r} . k_{c0+c} over D dimensions.  Lane l
-// supplies row / column l % 16 and dimensions by l / 16; it receives
-// S[4 (l / 16) + e][l % 16], e = 0..3.
-template <typename T, int D>
-__device__ __forceinline__ f32x4 logit_tile(const T* qrow, const T* krow) {
-    const int quarter = threadIdx.x / 16;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int kk = 0; kk < D; kk += 16) {
-            const bf16x4 a = *reinterpret_cast<const bf16x4*>(qrow + kk + 4 * quarter);
-            const bf16x4 b = *reinterpret_cast<const bf16x4*>(krow + kk + 4 * quarter);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < D; kk += 4) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[kk + quarter], krow[kk + quarter], acc, 0, 0, 0);
-        }
-    }
-    return acc;
+template <typename T>
+struct MfmaIn;
+template <>
+struct MfmaIn<uint16_t> {  // bf16: 16 dimensions per step, 4 per lane
+    using Op = bf16x4;
+    static constexpr int STEP = 16, PER = 4;
+    __device__ static Op load(const uint16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+    __device__ static f32x4 mfma(Op a, Op b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
+};
+template <>
+struct MfmaIn<float> {  // fp32: 4 dimensions per step, 1 per lane
+    using Op = float;
+    static constexpr int STEP = 4, PER = 1;
+    __device__ static Op load(const float* p) { return *p; }
+    __device__ static f32x4 mfma(Op a, Op b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+};
+
+// Merge two base-2 online-softmax states (max, sum); -inf max = empty.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn);
+    const float b = m2 == -INFINITY ? 0.0f : s2 * __builtin_amdgcn_exp2f(m2 - mn);
+    m = mn;
+    s = a + b;
 }
 
-// Reductions over the 16 lanes that hold one query's tile columns.
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
 __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
     return v;
 }
 
+// Each wavefront of a workgroup takes 16 consecutive queries (kMapWaves x 16
+// per workgroup); the 16-key tiles of K are staged in LDS once per
+// workgroup (coalesced 16-byte loads) and read by every wavefront.  Lane l
+// supplies tile row / column l % 16 and dimensions by l / 16 of each MFMA
+// step; it receives S[4 (l / 16) + e][l % 16], e = 0..3.
+constexpr int kMapWaves = 4;
+
 template <typename T, int D>
-__global__ void __launch_bounds__(64) profile_map_kernel(ProfileArgs a) {
-    const int tiles = (a.T + 15) / 16;
+__global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs a) {
+    using M = MfmaIn<T>;
+    constexpr int NS = D / M::STEP;
+    constexpr int ROWB = D * (int)sizeof(T);        // bytes of a key row
+    constexpr int RCH = ROWB / 16;                  // 16-byte chunks of a key row
+    constexpr int KCH = 16 * RCH;                   // ... of a 16-key tile
+    constexpr int PSTR = RCH + 1;                   // padded LDS row stride in chunks: rows 16 B apart in banks
+    const int tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
     const int lane = blockIdx.x / tiles;
-    const int i0 = (blockIdx.x % tiles) * 16;
-    const int l = threadIdx.x;
+    const int wave = threadIdx.x / 64;
+    const int i0 = (blockIdx.x % tiles) * 16 * kMapWaves + 16 * wave;  // this wavefront's first query
+    const int l = threadIdx.x % 64;
     const int col = l % 16, quarter = l / 16;
     const int b = lane / a.H, h = lane % a.H;
     const T* q = reinterpret_cast<const T*>(a.q);
     const T* k = reinterpret_cast<const T*>(a.k);
     const T* kp = reinterpret_cast<const T*>(a.k_p);
-    // A operand row: query i0 + col (rows past T repeat T - 1 and are not stored)
-    const T* qrow = q + (((size_t)min(i0 + col, a.T - 1) * a.B + b) * a.H + h) * D;
-    auto key_row = [&](int c) {  // key c: prompt row, then decode position c - L_p
-        return c < a.L_p ? kp + (((size_t)b * a.L_p + c) * a.H + h) * D
-                         : k + (((size_t)(c - a.L_p) * a.B + b) * a.H + h) * D;
+    __shared__ uint4 s_kt[16 * PSTR];  // the current 16-key tile, key-major
+    const T* s_k = reinterpret_cast<const T*>(s_kt);
+    // the query operand: row i0 + col (rows past T repeat T - 1 and are not stored)
+    typename M::Op qa[NS];
+    {
+        const T* qrow = q + (((size_t)min(i0 + col, a.T - 1) * a.B + b) * a.H + h) * D + M::PER * quarter;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qa[s] = M::load(qrow + s * M::STEP);
+    }
+    const int ncols = a.L_p + min((blockIdx.x % tiles) * 16 * kMapWaves + 16 * kMapWaves, a.T);  // keys of the group
+    auto stage = [&](int c0) {  // keys c0 .. c0 + 15 (past the last key: repeats it)
+        __syncthreads();
+        for (int x = threadIdx.x; x < KCH; x += 64 * kMapWaves) {
+            const int kk = x / RCH, part = x % RCH;
+            const int c = min(c0 + kk, ncols - 1);
+            const T* krow = c < a.L_p ? kp + (((size_t)b * a.L_p + c) * a.H + h) * D
+                                      : k + (((size_t)(c - a.L_p) * a.B + b) * a.H + h) * D;
+            s_kt[kk * PSTR + part] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(krow) + part * 16);
+        }
+        __syncthreads();
+    };
+    auto tile = [&]() {  // logits of the wavefront's 16 queries against the staged keys
+        const T* krow = s_k + col * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = M::mfma(qa[s], M::load(krow + s * M::STEP), acc);
+        return acc;
     };
     const float scale = (float)(1.4426950408889634 / sqrt((double)D));  // log2(e) / sqrt(D)
-    const int ncols = a.L_p + min(i0 + 16, a.T);                         // keys any of the 16 queries sees
 
-    // pass 1: online (max, sum) in base 2 for the 4 queries 4 quarter + e
+    // pass 1: this lane's online (max, sum) per query over its columns, then
+    // the 16 lanes of each query merged
     float m[4], s[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -91,34 +136,39 @@ __global__ void __launch_bounds__(64) profile_map_kernel(ProfileArgs a) {
         s[e] = 0.0f;
     }
     for (int c0 = 0; c0 < ncols; c0 += 16) {
+        stage(c0);
         const int c = c0 + col;
-        const f32x4 t = logit_tile<T, D>(qrow, key_row(min(c, ncols - 1)));
+        const f32x4 t = tile();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = i0 + 4 * quarter + e;
-            const bool ok = c < ncols && c <= a.L_p + i;  // causal: keys up to decode position i
-            const float x = ok ? t[e] * scale : -INFINITY;
-            const float mn = fmaxf(m[e], max16(x));
-            const float add = sum16(ok ? exp2f(x - mn) : 0.0f);
-            s[e] = (m[e] == -INFINITY ? 0.0f : s[e] * exp2f(m[e] - mn)) + add;
-            m[e] = mn;
+            if (c < ncols && c <= a.L_p + i) merge_ms(m[e], s[e], t[e] * scale, 1.0f);  // causal keys only
         }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) merge_ms(m[e], s[e], __shfl_xor(m[e], o), __shfl_xor(s[e], o));
     }
 
     // pass 2: probabilities of the decode keys and the mass split
     float* P = a.P + (size_t)lane * a.T * a.T;
     float mp[4] = {0, 0, 0, 0}, ml[4] = {0, 0, 0, 0}, mm[4] = {0, 0, 0, 0};
+    float inv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) inv[e] = 1.0f / s[e];
     for (int c0 = 0; c0 < ncols; c0 += 16) {
+        stage(c0);
         const int c = c0 + col;
-        const f32x4 t = logit_tile<T, D>(qrow, key_row(min(c, ncols - 1)));
+        const f32x4 t = tile();
+        const int j = c - a.L_p;  // decode position of the key
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = i0 + 4 * quarter + e;
             const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
-            const float p = ok ? exp2f(t[e] * scale - m[e]) / s[e] : 0.0f;
-            const int j = c - a.L_p;  // decode position of the key
-            const int n_loc = (i + 10) / 10;
-            mp[e] += c < a.L_p ? p : 0.0f;
+            const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
+            const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
+            mp[e] += j < 0 ? p : 0.0f;
             ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
             mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
             if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
@@ -137,87 +187,171 @@ __global__ void __launch_bounds__(64) profile_map_kernel(ProfileArgs a) {
     }
 }
 
+constexpr int kGramWaves = 4;  // row tiles per workgroup (one per wavefront)
+constexpr int kGramJ = 4;      // column tiles per pass (accumulators: 4 products x 4 tiles)
+constexpr int kGChunk = 32;    // staged columns per LDS chunk
+constexpr int kGStride = kGChunk + 1;
+
+// Stage columns [k0, k0 + kGChunk) of nrows rows r0.. of the map into LDS,
+// as P (row-major, zero beyond the causal part and past T) and as Q (offset
+// coordinates: Q[r][o] = P[r][r - o], zero for o > r).
+__device__ __forceinline__ void stage_rows(const float* P, int T, int r0, int nrows, int k0, float* sP, float* sQ) {
+    for (int x = threadIdx.x; x < nrows * kGChunk; x += 64 * kGramWaves) {
+        const int rr = x / kGChunk, kk = x % kGChunk;
+        const int r = r0 + rr, kx = k0 + kk;
+        const bool ok = r < T && kx <= r;
+        sP[rr * kGStride + kk] = ok ? P[(size_t)r * T + kx] : 0.0f;
+        sQ[rr * kGStride + kk] = ok ? P[(size_t)r * T + (r - kx)] : 0.0f;
+    }
+}
+
+// A workgroup takes 64 rows I0 .. I0+63, wavefront w the row tile I = I0 +
+// 16 w.  A pass covers the column tiles J = I + 64 g + 16 c (c < 4) of every
+// wavefront: their rows, I0 + 64 g .. I0 + 64 g + 111, are staged once per
+// chunk for all four wavefronts (pass 0 holds the A rows among them; later
+// passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 x 33 floats.
+__global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileArgs a) {
+    // blockIdx -> (lane, row block) with all row blocks of a lane on one XCD
+    // (workgroup x runs on XCD x % 8; lanes are padded to a multiple of 8):
+    // they reread the lane's map from one L2.
+    const int tiles = (a.T + 15) / 16;
+    const int blocks = (tiles + kGramWaves - 1) / kGramWaves;
+    const int x = blockIdx.x;
+    const int lane = (x % 8) + 8 * (x / (8 * blocks));
+    const int bi = (x / 8) % blocks;
+    if (lane >= a.lanes) return;
+    const int I0 = bi * 16 * kGramWaves;
+    const int wave = threadIdx.x / 64, l = threadIdx.x % 64, col = l % 16, quarter = l / 16;
+    const int I = I0 + 16 * wave;
+    const float* P = a.P + (size_t)lane * a.T * a.T;
+
+    constexpr int NB = 16 * (kGramWaves + kGramJ - 1);  // B rows of a pass: 112
+    extern __shared__ float s_dyn[];
+    float* sPB = s_dyn;
+    float* sQB = sPB + NB * kGStride;
+    float* sPA = sQB + NB * kGStride;  // later passes only
+    float* sQA = sPA + 16 * kGramWaves * kGStride;
+    __shared__ double s_sum[2 * kMaxProfileDist];  // per distance: vertical, diagonal
+    __shared__ float s_na[16 * kGramWaves];        // |P[i][0..i]|^2 of the block's rows
+    for (int d = threadIdx.x; d < 2 * a.max_dist; d += 64 * kGramWaves) s_sum[d] = 0.0;
+
+    const int kend = min(I0 + 16 * kGramWaves, a.T);                 // P[i][k] = 0 for k > i
+    const int span = 15 + a.max_dist;                                // columns i' - I needed: 0 .. span
+    const int passes = span / (16 * kGramJ) + 1;
+    for (int g = 0; g < passes; ++g) {
+        const int J0 = I + 16 * kGramJ * g;  // this wavefront's first column tile of the pass
+        f32x4 gv[kGramJ], gd[kGramJ], nb[kGramJ], nc[kGramJ];
+#pragma unroll
+        for (int c = 0; c < kGramJ; ++c) gv[c] = gd[c] = nb[c] = nc[c] = f32x4{0, 0, 0, 0};
+        const float* pA = g == 0 ? sPB : sPA;  // the A rows: inside the pass-0 B rows
+        const float* qA = g == 0 ? sQB : sQA;
+        const int aoff = 16 * wave;            // this wavefront's A rows in that buffer
+        for (int k0 = 0; k0 < kend; k0 += kGChunk) {
+            __syncthreads();
+            stage_rows(P, a.T, I0 + 16 * kGramJ * g, NB, k0, sPB, sQB);
+            if (g > 0) stage_rows(P, a.T, I0, 16 * kGramWaves, k0, sPA, sQA);
+            __syncthreads();
+            if (I < a.T) {
+                const int kc = min(kGChunk, kend - k0);
+                for (int kk = 0; kk < kc; kk += 4) {
+                    const int kl = kk + quarter;                               // this lane's column in the step
+                    const float pa = pA[(aoff + col) * kGStride + kl];          // A[row = col][k]
+                    const float qa = qA[(aoff + col) * kGStride + kl];
+                    const float ind = (k0 + kl <= I + col) ? 1.0f : 0.0f;       // L[I + col][k]
+#pragma unroll
+                    for (int c = 0; c < kGramJ; ++c) {
+                        const int rb = 16 * (wave + c) + col;                   // B row J0 + 16 c + col
+                        const float pb = sPB[rb * kGStride + kl];
+                        const float qb = sQB[rb * kGStride + kl];
+                        gv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, pb, gv[c], 0, 0, 0);
+                        gd[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, qb, gd[c], 0, 0, 0);
+                        nb[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, pb * pb, nb[c], 0, 0, 0);
+                        nc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, qb * qb, nc[c], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // lane holds entries (i, i') = (I + 4 quarter + e, J0 + 16 c + col)
+        if (g == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * quarter + e == col) s_na[16 * wave + col] = gv[0][e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kGramJ; ++c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = I + 4 * quarter + e, ip = J0 + 16 * c + col, d = ip - i;
+                if (i < a.T && ip < a.T && d >= 1 && d <= a.max_dist) {
+                    const double na = s_na[16 * wave + 4 * quarter + e];
+                    atomicAdd(&s_sum[2 * (d - 1)], (double)gv[c][e] / sqrt(na * (double)nb[c][e]));
+                    atomicAdd(&s_sum[2 * (d - 1) + 1], (double)gd[c][e] / sqrt(na * (double)nc[c][e]));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // one partial row per 16-row tile keeps the reduce kernel's layout: the
+    // block's sums go to its first tile, the others are zero
+    const int nt = min(kGramWaves, tiles - bi * kGramWaves);
+    for (int t = 0; t < nt; ++t) {
+        double* part = a.partial + ((size_t)lane * tiles + bi * kGramWaves + t) * 2 * a.max_dist;
+        for (int d = threadIdx.x; d < 2 * a.max_dist; d += 64 * kGramWaves) part[d] = t == 0 ? s_sum[d] : 0.0;
+    }
+}
+
+size_t gram_lds_bytes(int max_dist) {
+    const int passes = (15 + max_dist) / (16 * kGramJ) + 1;
+    const int rows = 16 * (kGramWaves + kGramJ - 1) + (passes > 1 ? 16 * kGramWaves : 0);
+    return (size_t)rows * 2 * kGStride * sizeof(float);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
 
-constexpr int kSimWaves = 4;
-
-__global__ void __launch_bounds__(64 * kSimWaves) profile_sim_kernel(ProfileArgs a) {
-    // blockIdx -> (lane, distance) with every distance of a lane on one XCD:
-    // block x goes to XCD x % 8; lanes are padded to a multiple of 8.
-    const int x = blockIdx.x;
-    const int lane = (x % 8) + 8 * (x / (8 * a.max_dist));
-    const int dd = 1 + (x / 8) % a.max_dist;
-    if (lane >= a.lanes) return;
-    const int wave = threadIdx.x / 64, wl = threadIdx.x % 64;
-    const float* P = a.P + (size_t)lane * a.T * a.T;
-    const int n = a.T - dd;
-    double sv = 0.0, sd = 0.0;
-    for (int i = wave; i < n; i += kSimWaves) {
-        const float* ra = P + (size_t)i * a.T;
-        const float* rb = P + (size_t)(i + dd) * a.T;
-        double ab = 0, ac = 0, aa = 0, bb = 0, cc = 0;
-        for (int j = wl; j <= i; j += 64) {
-            const double va = ra[j], vb = rb[j], vc = rb[j + dd];
-            ab += va * vb;
-            ac += va * vc;
-            aa += va * va;
-            bb += vb * vb;
-            cc += vc * vc;
-        }
-        ab = wave_sum_d(ab);
-        ac = wave_sum_d(ac);
-        aa = wave_sum_d(aa);
-        bb = wave_sum_d(bb);
-        cc = wave_sum_d(cc);
-        sv += ab / sqrt(aa * bb);
-        sd += ac / sqrt(aa * cc);
+__global__ void __launch_bounds__(64) profile_reduce_kernel(ProfileArgs a) {
+    const int lane = blockIdx.x;
+    const int l = threadIdx.x;
+    const int tiles = (a.T + 15) / 16;
+    const double* part = a.partial + (size_t)lane * tiles * 2 * a.max_dist;
+    for (int x = l; x < 2 * a.max_dist; x += 64) {
+        double sum = 0.0;
+        for (int t = 0; t < tiles; ++t) sum += part[(size_t)t * 2 * a.max_dist + x];
+        const int d = x / 2 + 1, n = a.T - d;
+        (x % 2 ? a.diag : a.vert)[(size_t)lane * a.max_dist + d - 1] = sum / n;
     }
-    __shared__ double s_v[kSimWaves], s_d[kSimWaves];
-    if (wl == 0) {
-        s_v[wave] = sv;
-        s_d[wave] = sd;
+    const float* r = a.mass_rows + (size_t)lane * a.T * 3;
+    double g[3] = {0, 0, 0};
+    for (int i = l; i < a.T; i += 64) {
+        g[0] += r[3 * i];
+        g[1] += r[3 * i + 1];
+        g[2] += r[3 * i + 2];
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double tv = 0, td = 0;
-        for (int w = 0; w < kSimWaves; ++w) {
-            tv += s_v[w];
-            td += s_d[w];
-        }
-        a.vert[(size_t)lane * a.max_dist + dd - 1] = n > 0 ? tv / n : NAN;
-        a.diag[(size_t)lane * a.max_dist + dd - 1] = n > 0 ? td / n : NAN;
-    }
-    if (dd == 1) {
-        // the lane's mean mass split over its queries
-        __syncthreads();
-        if (wave == 0) {
-            const float* r = a.mass_rows + (size_t)lane * a.T * 3;
-            double g[3] = {0, 0, 0};
-            for (int i = wl; i < a.T; i += 64) {
-                g[0] += r[3 * i];
-                g[1] += r[3 * i + 1];
-                g[2] += r[3 * i + 2];
-            }
-            for (int c = 0; c < 3; ++c) {
-                const double v = wave_sum_d(g[c]);
-                if (wl == 0) a.mass[(size_t)lane * 3 + c] = v / a.T;
-            }
-        }
+    for (int c = 0; c < 3; ++c) {
+        const double v = wave_sum_d(g[c]);
+        if (l == 0) a.mass[(size_t)lane * 3 + c] = v / a.T;
     }
 }
 
 template <typename T, int D>
 hipError_t launch_profile_t(const ProfileArgs& a, hipStream_t s) {
     const int tiles = (a.T + 15) / 16;
-    hipLaunchKernelGGL((profile_map_kernel<T, D>), dim3((unsigned)((long long)a.lanes * tiles)), dim3(64), 0, s, a);
+    const int map_tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
+    hipLaunchKernelGGL((profile_map_kernel<T, D>), dim3((unsigned)((long long)a.lanes * map_tiles)),
+                       dim3(64 * kMapWaves), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long lanes8 = ((long long)a.lanes + 7) / 8 * 8;
-    hipLaunchKernelGGL(profile_sim_kernel, dim3((unsigned)(lanes8 * a.max_dist)), dim3(64 * kSimWaves), 0, s, a);
+    const int blocks = (tiles + kGramWaves - 1) / kGramWaves;
+    hipLaunchKernelGGL(profile_gram_kernel, dim3((unsigned)(lanes8 * blocks)), dim3(64 * kGramWaves),
+                       gram_lds_bytes(a.max_dist), s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(profile_reduce_kernel, dim3((unsigned)a.lanes), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -433,7 +433,7 @@ def characterize(w, inputs, dev, max_dist, reps=3):
     x = inputs.layers[0]
     B, H, D, L, T = w.batch, w.heads, w.head_dim, w.L_p, w.L_dec
     lanes = B * H
-    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L, T)
+    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L, T, max_dist)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     mass = torch.empty((lanes, 3), dtype=torch.float64, device=dev)
     vert = torch.empty((lanes, max_dist), dtype=torch.float64, device=dev)

@@ -246,12 +246,13 @@ int dsa_set_waves(dsa_state* st, int waves_per_lane);
  *                      probabilities (prompt columns left out).
  * q, k: [T][batch][heads][head_dim], k_p: [batch][L_p][heads][head_dim], in
  * dtype DSA_F32 or DSA_BF16, 16-byte aligned.  Outputs: device fp64 arrays,
- * 8-byte aligned.  1 <= max_dist <= T - 1.  The workspace (size from
- * dsa_profile_workspace_bytes, 256-byte aligned) holds the fp32 map
- * [lanes][T][T] and per-query mass; it is the caller's.  Asynchronous on
- * hip_stream (NULL = null stream).  The logits are MFMA tiles (fp32 sums).
+ * 8-byte aligned.  1 <= max_dist <= min(T - 1, 256).  The workspace (size
+ * from dsa_profile_workspace_bytes, 256-byte aligned) holds the fp32 map
+ * [lanes][T][T], the per-query mass and per-tile sums; it is the caller's.
+ * Asynchronous on hip_stream (NULL = null stream).  The logits and the
+ * similarity dot products are MFMA tiles with fp32 sums; the means are fp64.
  */
-size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T);
+size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T, int max_dist);
 int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
                           int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
                           double* vert, double* diag, void* hip_stream);

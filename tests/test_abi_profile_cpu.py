@@ -1,0 +1,57 @@
+"""Host-side checks of the characterization entry points (no GPU): workspace
+size and argument validation before anything is enqueued."""
+import pytest
+
+import autoregressive_image_generation_amd as dsa
+from autoregressive_image_generation_amd import DsaError
+
+FAKE = 1 << 40  # aligned addresses never dereferenced here
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,L_p,T,dmax", [(96, 32, 64, 576, 48), (1, 4, 16, 64, 20), (2, 1, 0, 37, 36)])
+def test_workspace_size(B, H, L_p, T, dmax):
+    lanes = B * H
+    want = _align(lanes * T * T * 4) + _align(lanes * T * 3 * 4) + _align(lanes * ((T + 15) // 16) * 2 * dmax * 8)
+    assert dsa.dsa_profile_workspace_bytes(B, H, L_p, T, dmax) == want
+
+
+@pytest.mark.parametrize("args", [
+    (0, 4, 16, 64, 8),     # batch 0
+    (1, 4, -1, 64, 8),     # negative prompt
+    (1, 4, 16, 1, 1),      # T < 2
+    (1, 4, 16, 64, 64),    # max_dist > T - 1
+    (1, 4, 16, 600, 257),  # max_dist beyond the LDS sums
+    (1, 4, 16, 64, 0),
+])
+def test_invalid_sizes(args):
+    assert dsa.dsa_profile_workspace_bytes(*args) == 0
+
+
+def _call(**kw):
+    a = dict(q=FAKE, k=FAKE, k_p=FAKE, batch=1, heads=4, head_dim=64, L_p=16, T=64, dtype=1, max_dist=8,
+             workspace=FAKE, workspace_bytes=1 << 40, mass=FAKE, vert=FAKE, diag=FAKE)
+    a.update(kw)
+    return dsa.dsa_attention_profile(a["q"], a["k"], a["k_p"], a["batch"], a["heads"], a["head_dim"], a["L_p"], a["T"],
+                                     a["dtype"], a["max_dist"], a["workspace"], a["workspace_bytes"], a["mass"],
+                                     a["vert"], a["diag"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -1),            # MXFP8 inputs are not a profile dtype
+    (dict(head_dim=96), -1),
+    (dict(max_dist=64), -1),
+    (dict(q=FAKE + 8), -1),         # misaligned input
+    (dict(k_p=None), -1),           # prompt keys missing with L_p > 0
+    (dict(vert=FAKE + 4), -1),      # misaligned output
+    (dict(mass=None), -1),
+    (dict(workspace=FAKE + 16), -3),
+    (dict(workspace_bytes=10), -3),
+])
+def test_invalid_calls_fail_before_launch(kw, code):
+    with pytest.raises(DsaError) as e:
+        _call(**kw)
+    assert e.value.code == code

@@ -30,7 +30,7 @@ def say(msg):
 
 def run_profile(q, k, kp, B, H, D, L_p, T, dtype, max_dist):
     lanes = B * H
-    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L_p, T)
+    nbytes = dsa.dsa_profile_workspace_bytes(B, H, L_p, T, max_dist)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     mass = torch.empty((lanes, 3), dtype=torch.float64, device=DEV)
     vert = torch.empty((lanes, max_dist), dtype=torch.float64, device=DEV)
