@@ -233,14 +233,19 @@ def test_full_size_workload_sampled_lanes(name):
     assert ok.all()
 
 
-@pytest.mark.parametrize("name", ["janus_pro_1b", "janus_pro_7b"])
+@pytest.mark.parametrize("name", ["janus_pro_1b", "janus_pro_7b", "lumina_mgpt_7b_1024", "hires_8100_sink4",
+                                  "janus_pro_7b+mxfp8"])
 def test_full_size_every_lane_of_one_layer(name):
-    """Every lane of one full layer (512 / 3072 lanes x 576 steps) in the
-    benchmarked launch shape against the oracle: exact choice and eviction
-    traces, outputs within the bf16 bound (lockstep per lane, in a thread pool)."""
+    """Every lane of one full layer (512 / 3072 / 512 / 256 lanes x all L_dec
+    steps) in the benchmarked launch shape against the oracle: exact choice
+    and eviction traces, outputs within the bf16 bound (lockstep per lane, in
+    a thread pool).  "+mxfp8": the same with the MXFP8 cache."""
     from concurrent.futures import ThreadPoolExecutor
 
-    w = synth.WORKLOADS[name]
+    base, _, kv = name.partition("+")
+    w = synth.WORKLOADS[base]
+    if kv == "mxfp8":
+        w = w.with_(dtype=synth.MXFP8)
     layer = 0
     T = w.L_dec
     say("every lane: %s layer %d (%d lanes)" % (name, layer, w.lanes))
@@ -251,8 +256,11 @@ def test_full_size_every_lane_of_one_layer(name):
 
     def one(lane):
         b, h = divmod(lane, w.heads)
-        li = tuple(oracle.widen(a, w.dtype) for a in (host["q"][:, b, h], host["kp"][b, :, h], host["vp"][b, :, h],
-                                                     host["k"][:, b, h], host["v"][:, b, h]))
+        q_, kp_, vp_, k_, v_ = (oracle.widen(a, w.input_dtype) for a in (
+            host["q"][:, b, h], host["kp"][b, :, h], host["vp"][b, :, h], host["k"][:, b, h], host["v"][:, b, h]))
+        if w.dtype == synth.MXFP8:  # the cache holds the K / V rows quantised
+            kp_, vp_, k_, v_ = (oracle.mxfp8_roundtrip(x) for x in (kp_, vp_, k_, v_))
+        li = (q_, kp_, vp_, k_, v_)
         st = {}
         check_lane(w, li, out[:, b, h, :], trace[:, b, h, :], st)
         return st
