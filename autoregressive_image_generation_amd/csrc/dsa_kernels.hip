@@ -41,10 +41,11 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 constexpr float kNegBig = -1.0e30f;
-#ifndef DSA_ROWS_PER_CHUNK
-#define DSA_ROWS_PER_CHUNK 4
-#endif
-constexpr int kRowsPerChunk = DSA_ROWS_PER_CHUNK;  // pipeline depth in rows per thread group
+// Pipeline depth in rows per thread group: 3 for one-wavefront workgroups
+// (large batches: many resident wavefronts per CU already keep HBM busy, and
+// the shallower pipeline frees registers), 4 otherwise.
+constexpr int kRowsPerChunkOneWave = 3;
+constexpr int kRowsPerChunk = 4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -456,14 +457,35 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             if (valid && sl == 0) s_logit[r] = s;
         }
         const float x = valid ? (float)(s * a.scale_log2e) : -__builtin_inff();
-        const float mn = fmaxf(sm.m, x);
-        const float c = __builtin_amdgcn_exp2f(sm.m - mn);
-        const float p = __builtin_amdgcn_exp2f(x - mn);
-        sm.l = sm.l * c + p;
-        const float pv = MX ? p * vscale : p;
+        if constexpr (MX) {
+            // 16 accumulators per thread: the running maximum moves only when
+            // a logit exceeds it by more than 8 (log2 units), so weights stay
+            // below 2^8 and the accumulators are rescaled only when some group
+            // of the wavefront needs it (the state (m, l, acc) stays exact for
+            // any m it holds)
+            const bool need = x > sm.m + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = need ? x : sm.m;
+                const float c = __builtin_amdgcn_exp2f(sm.m - mn);
+                sm.l *= c;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + pv * vf[e];
-        sm.m = mn;
+                for (int e = 0; e < EPT; ++e) acc[e] *= c;
+                sm.m = mn;
+            }
+            const float p = __builtin_amdgcn_exp2f(x - sm.m);
+            sm.l += p;
+            const float pv = p * vscale;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) acc[e] = fmaf(pv, vf[e], acc[e]);
+        } else {
+            const float mn = fmaxf(sm.m, x);
+            const float c = __builtin_amdgcn_exp2f(sm.m - mn);
+            const float p = __builtin_amdgcn_exp2f(x - mn);
+            sm.l = sm.l * c + p;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + p * vf[e];
+            sm.m = mn;
+        }
     };
 
     // Rolling pipeline: consume row k from its buffer, then refill that buffer
@@ -799,9 +821,8 @@ __global__ void prompt_kernel(PromptArgs a) {
     }
 }
 
-template <typename F, int D>
-hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
-    constexpr int U = kRowsPerChunk;
+template <typename F, int D, int U>
+hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
     constexpr int TPR = D / F::EPT;
     const int G = waves * (64 / TPR);
     dim3 grid(a.lanes), block(64 * waves);
@@ -835,6 +856,12 @@ hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t
         }
     }
     return hipGetLastError();
+}
+
+template <typename F, int D>
+hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
+    return waves == 1 ? launch_decode_u<F, D, kRowsPerChunkOneWave>(mode, waves, a, s)
+                      : launch_decode_u<F, D, kRowsPerChunk>(mode, waves, a, s);
 }
 
 template <typename F, int D>
