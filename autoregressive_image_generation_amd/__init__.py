@@ -28,6 +28,7 @@ from .binding import (
     dsa_append_kv,
     dsa_append_prompt,
     dsa_attention_profile,
+    dsa_hbm_read_probe,
     dsa_decode_step,
     dsa_last_error,
     dsa_policy_state_init,

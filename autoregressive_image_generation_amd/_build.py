@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("dsa_api.hip", "dsa_kernels.hip", "dsa_profile.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("dsa_api.hip", "dsa_kernels.hip", "dsa_profile.hip", "dsa_probe.hip")]
 HEADERS = [os.path.join(ROOT, "include", "dsa.h"), os.path.join(HERE, "csrc", "dsa_internal.h")]
 
 HIPCC_FLAGS = [

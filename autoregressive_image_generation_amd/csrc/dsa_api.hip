@@ -632,6 +632,22 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
     return DSA_OK;
 }
 
+int dsa_hbm_read_probe(const void* src, size_t bytes, int blocks, int threads, int unroll, uint32_t* sink,
+                       void* hip_stream) {
+    if (!src || !sink) return fail(DSA_E_INVAL, "src / sink is NULL");
+    if (bytes == 0 || bytes % 16 != 0) return fail(DSA_E_INVAL, "bytes must be a positive multiple of 16");
+    if (!aligned16(src)) return fail(DSA_E_INVAL, "src must be 16-byte aligned");
+    if ((uintptr_t)sink & 3u) return fail(DSA_E_INVAL, "sink must be 4-byte aligned");
+    if (blocks < 1 || blocks > 65536) return fail(DSA_E_INVAL, "blocks must be in [1, 65536] (got %d)", blocks);
+    if (threads < 64 || threads > 1024 || threads % 64 != 0)
+        return fail(DSA_E_INVAL, "threads must be a multiple of 64 in [64, 1024] (got %d)", threads);
+    if (unroll != 1 && unroll != 4 && unroll != 8) return fail(DSA_E_INVAL, "unroll must be 1, 4 or 8 (got %d)", unroll);
+    hipError_t e = dsa::launch_hbm_read_probe(src, bytes, blocks, threads, unroll, sink,
+                                              static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return DSA_OK;
+}
+
 int dsa_set_waves(dsa_state* st, int waves_per_lane) {
     int rc = check_state(st, 0);
     if (rc) return rc;

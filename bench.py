@@ -73,6 +73,7 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
     p.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 KV-cache leg")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
     p.add_argument("--profile-dist", type=int, default=48,
                    help="attention-map characterization of layer 0 up to this query distance (0: skip)")
     p.add_argument("--no-policies", action="store_true",
@@ -421,6 +422,39 @@ def kernel_durations(model, layers, dev):
     return per_step
 
 
+def hbm_read_ceiling(dev, nbytes=4 << 30, reps=10):
+    """Practical HBM read ceiling: the library's read probe (16-byte non-temporal
+    loads, grid-stride) over a 4 GiB buffer, best of a few launch shapes."""
+    import torch
+
+    import autoregressive_image_generation_amd as dsa
+
+    src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        for threads in (256, 512):
+            for unroll in (4, 8):
+                def run():
+                    dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, unroll, sink, stream)
+                run()
+                start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                start.record(stream)
+                for _ in range(reps):
+                    run()
+                stop.record(stream)
+                torch.cuda.synchronize(dev)
+                gbs = nbytes * reps / (start.elapsed_time(stop) * 1e-3) / 1e9
+                if best is None or gbs > best["GBs"]:
+                    best = {"GBs": gbs, "blocks": blocks, "threads": threads, "unroll": unroll}
+    if int(sink.item()) != 0:
+        raise RuntimeError("read probe: the sink was written for a zero buffer")
+    del src
+    torch.cuda.empty_cache()
+    return best
+
+
 def characterize(w, inputs, dev, max_dist, reps=3):
     """Section 3.4 measurements (Figs. 8 and 10) on the dense decode map of
     layer 0, all lanes: mean mass split and vertical / diagonal similarity,
@@ -620,6 +654,13 @@ def main():
                                                  ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
         if hi > lo:
             phase_us[name] = sum(sum(durs[t]) for t in range(lo, hi)) / ((hi - lo) * layers) * 1e6
+    # per-step latency as the window fills and slides: the mean launch over the
+    # layers at ~48 evenly spaced steps (and the phase boundaries)
+    step_series = None
+    if durs is not None:
+        marks = set(range(0, w.L_dec, max(1, w.L_dec // 48))) | {w.L_dec - 1}
+        marks |= {t for t in (w.N_att - 2, w.N_att - 1, w.N_r - 1, w.N_r) if 0 <= t < w.L_dec}
+        step_series = [[t, round(sum(durs[t]) / layers * 1e6, 3)] for t in sorted(marks)]
 
     result = {
         "metric": "sparse decode-attn steps/s (batch x layers x heads) + HBM GB/s, Janus-Pro-7B shape",
@@ -647,7 +688,8 @@ def main():
                      "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
                      "avg_launch_us": launch_s * 1e6,
                      "bytes_per_launch": bytes_per_launch,
-                     "event_pair_us_by_phase": phase_us},
+                     "event_pair_us_by_phase": phase_us,
+                     "event_pair_us_by_step": step_series},
         "events_ms_per_step": sec_ev * 1e3,
     }
     if S > 1:
@@ -725,6 +767,16 @@ def main():
             log("sweep %.2f: %.1f ms" % (sp, s * 1e3))
             del m
         result["sweep"] = sweep
+
+    if not args.no_ceiling:
+        c = hbm_read_ceiling(dev)
+        result["hbm_read_ceiling"] = {
+            "kernel": "dsa_hbm_read_probe (16-byte non-temporal loads, grid-stride, 4 GiB, best launch shape)",
+            "GBs": c["GBs"], "frac_of_peak": c["GBs"] / HBM_PEAK_GBS,
+            "shape": {k: c[k] for k in ("blocks", "threads", "unroll")},
+            "sparse_one_stream_frac_of_ceiling": achieved / c["GBs"],
+            "sparse_micro_batched_frac_of_ceiling": (total_bytes / sec_ev / 1e9) / c["GBs"] if S > 1 else None}
+        log("hbm read ceiling: %.0f GB/s (%s)" % (c["GBs"], result["hbm_read_ceiling"]["shape"]))
 
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle) ...")

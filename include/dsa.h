@@ -257,6 +257,21 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
                           int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
                           double* vert, double* diag, void* hip_stream);
 
+/*
+ * HBM read probe (a measurement utility, not part of the method): streams
+ * `bytes` from src once with 16-byte non-temporal loads, grid-stride over
+ * `blocks` workgroups of `threads`, `unroll` loads in flight per thread, the
+ * way the decode kernels stream their cache rows.  Gives the practical read
+ * ceiling of the device that the decode kernels' bandwidth is read against.
+ * src: device, 16-byte aligned, bytes a positive multiple of 16.  sink: one
+ * device uint32, written only if a thread's XOR of the words it read equals
+ * 0x9e3779b9 (which keeps the loads from being optimised out).  blocks in
+ * [1, 65536]; threads a multiple of 64 in [64, 1024]; unroll 1, 4 or 8.
+ * Asynchronous on hip_stream; DSA_E_INVAL on bad arguments (nothing launched).
+ */
+int dsa_hbm_read_probe(const void* src, size_t bytes, int blocks, int threads, int unroll, uint32_t* sink,
+                       void* hip_stream);
+
 /* Next step index of a sparse or dense state (or a negative dsa_status). */
 int dsa_state_step(const dsa_state* st);
 

@@ -55,3 +55,20 @@ def test_invalid_calls_fail_before_launch(kw, code):
     with pytest.raises(DsaError) as e:
         _call(**kw)
     assert e.value.code == code
+
+
+def _probe(**kw):
+    a = dict(src=FAKE, nbytes=1 << 20, blocks=1024, threads=256, unroll=8, sink=FAKE)
+    a.update(kw)
+    return dsa.dsa_hbm_read_probe(a["src"], a["nbytes"], a["blocks"], a["threads"], a["unroll"], a["sink"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(src=None), dict(sink=None), dict(src=FAKE + 8), dict(sink=FAKE + 2),
+    dict(nbytes=0), dict(nbytes=24), dict(blocks=0), dict(blocks=65537),
+    dict(threads=32), dict(threads=96), dict(threads=2048), dict(unroll=2), dict(unroll=0),
+])
+def test_read_probe_rejects_bad_arguments_before_launch(kw):
+    with pytest.raises(DsaError) as e:
+        _probe(**kw)
+    assert e.value.code == -1
