@@ -19,6 +19,10 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed fp32 VALU forms stay off: all fp32 math goes through scalar forms
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: without it the characterization
+    # kernels' accumulators are copied between AGPRs and VGPRs around every
+    # MFMA step (the decode kernels use no MFMA; their code is unchanged)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -24,8 +24,9 @@
 // four wavefronts takes 64 rows; each wavefront computes the 16 x 16 tiles
 // of the four products for its 16 rows and the columns i + 1 .. i +
 // max_dist with MFMA (v_mfma_f32_16x16x4_f32), four column tiles per pass,
-// from 32-column chunks of the rows staged once for all four wavefronts in
-// LDS (padded stride: no bank conflicts), and adds each cosine into
+// from 16-column chunks of the rows staged once for all four wavefronts in
+// LDS (padded stride: no bank conflicts; the next chunk is loaded into
+// registers while the current one is consumed), and adds each cosine into
 // per-distance sums.
 // profile_reduce_kernel: per lane, the sums over row tiles in order, the
 // means, and the mean mass split.
@@ -189,27 +190,53 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
 
 constexpr int kGramWaves = 4;  // row tiles per workgroup (one per wavefront)
 constexpr int kGramJ = 4;      // column tiles per pass (accumulators: 4 products x 4 tiles)
-constexpr int kGChunk = 32;    // staged columns per LDS chunk
+constexpr int kGChunk = 16;    // staged columns per LDS chunk (its prefetch registers still fit 3 waves per SIMD)
 constexpr int kGStride = kGChunk + 1;
 
-// Stage columns [k0, k0 + kGChunk) of nrows rows r0.. of the map into LDS,
-// as P (row-major, zero beyond the causal part and past T) and as Q (offset
-// coordinates: Q[r][o] = P[r][r - o], zero for o > r).
-__device__ __forceinline__ void stage_rows(const float* P, int T, int r0, int nrows, int k0, float* sP, float* sQ) {
-    for (int x = threadIdx.x; x < nrows * kGChunk; x += 64 * kGramWaves) {
-        const int rr = x / kGChunk, kk = x % kGChunk;
-        const int r = r0 + rr, kx = k0 + kk;
-        const bool ok = r < T && kx <= r;
-        sP[rr * kGStride + kk] = ok ? P[(size_t)r * T + kx] : 0.0f;
-        sQ[rr * kGStride + kk] = ok ? P[(size_t)r * T + (r - kx)] : 0.0f;
+// Columns [k0, k0 + kGChunk) of NROWS rows r0.. of the map, as P (row-major,
+// zero beyond the causal part and past T) and as Q (offset coordinates:
+// Q[r][o] = P[r][r - o], zero for o > r), held in registers: element x of
+// the chunk (row x / kGChunk, column x % kGChunk) is thread x mod 256's
+// entry x / 256, so a wavefront reads two 128-byte row segments per entry.
+template <int NROWS>
+struct Staged {
+    static constexpr int RSTEP = 64 * kGramWaves / kGChunk;  // rows between a thread's entries: 8
+    static constexpr int N = NROWS / RSTEP;
+    static_assert(NROWS % RSTEP == 0 && 64 * kGramWaves % kGChunk == 0, "whole entries per thread");
+    float p[N], q[N];
+
+    // Issue the loads (they complete while the current chunk is consumed).
+    // Thread x holds column kk = x % kGChunk of rows x / kGChunk + RSTEP n.
+    __device__ __forceinline__ void load(const float* P, int T, int r0, int k0) {
+        const int rr = threadIdx.x / kGChunk, kx = k0 + threadIdx.x % kGChunk;
+        int r = r0 + rr;
+        const float* pp = P + (size_t)r * T + kx;       // P[r][kx]
+        const float* pq = P + (size_t)r * T + (r - kx);  // P[r][r - kx]
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const bool ok = r < T && kx <= r;
+            p[n] = ok ? *pp : 0.0f;
+            q[n] = ok ? *pq : 0.0f;
+            r += RSTEP;
+            pp += (size_t)RSTEP * T;
+            pq += (size_t)RSTEP * (T + 1);
+        }
     }
-}
+    __device__ __forceinline__ void store(float* sP, float* sQ) const {
+        const int off = (threadIdx.x / kGChunk) * kGStride + threadIdx.x % kGChunk;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            sP[off + n * RSTEP * kGStride] = p[n];
+            sQ[off + n * RSTEP * kGStride] = q[n];
+        }
+    }
+};
 
 // A workgroup takes 64 rows I0 .. I0+63, wavefront w the row tile I = I0 +
 // 16 w.  A pass covers the column tiles J = I + 64 g + 16 c (c < 4) of every
 // wavefront: their rows, I0 + 64 g .. I0 + 64 g + 111, are staged once per
 // chunk for all four wavefronts (pass 0 holds the A rows among them; later
-// passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 x 33 floats.
+// passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 x 17 floats.
 __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileArgs a) {
     // blockIdx -> (lane, row block) with all row blocks of a lane on one XCD
     // (workgroup x runs on XCD x % 8; lanes are padded to a multiple of 8):
@@ -246,11 +273,21 @@ __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileAr
         const float* pA = g == 0 ? sPB : sPA;  // the A rows: inside the pass-0 B rows
         const float* qA = g == 0 ? sQB : sQA;
         const int aoff = 16 * wave;            // this wavefront's A rows in that buffer
+        // the next chunk's rows are loaded into registers while this one is
+        // consumed from LDS
+        Staged<NB> nxB;
+        Staged<16 * kGramWaves> nxA;
+        nxB.load(P, a.T, I0 + 16 * kGramJ * g, 0);
+        if (g > 0) nxA.load(P, a.T, I0, 0);
         for (int k0 = 0; k0 < kend; k0 += kGChunk) {
             __syncthreads();
-            stage_rows(P, a.T, I0 + 16 * kGramJ * g, NB, k0, sPB, sQB);
-            if (g > 0) stage_rows(P, a.T, I0, 16 * kGramWaves, k0, sPA, sQA);
+            nxB.store(sPB, sQB);
+            if (g > 0) nxA.store(sPA, sQA);
             __syncthreads();
+            if (k0 + kGChunk < kend) {
+                nxB.load(P, a.T, I0 + 16 * kGramJ * g, k0 + kGChunk);
+                if (g > 0) nxA.load(P, a.T, I0, k0 + kGChunk);
+            }
             if (I < a.T) {
                 const int kc = min(kGChunk, kend - k0);
                 for (int kk = 0; kk < kc; kk += 4) {
@@ -284,9 +321,11 @@ __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileAr
             for (int e = 0; e < 4; ++e) {
                 const int i = I + 4 * quarter + e, ip = J0 + 16 * c + col, d = ip - i;
                 if (i < a.T && ip < a.T && d >= 1 && d <= a.max_dist) {
-                    const double na = s_na[16 * wave + 4 * quarter + e];
-                    atomicAdd(&s_sum[2 * (d - 1)], (double)gv[c][e] / sqrt(na * (double)nb[c][e]));
-                    atomicAdd(&s_sum[2 * (d - 1) + 1], (double)gd[c][e] / sqrt(na * (double)nc[c][e]));
+                    // fp32 cosines of the fp32 sums (v_rsq_f32 is within about
+                    // one ulp, far below the sums' own rounding); fp64 means
+                    const float ra = __builtin_amdgcn_rsqf(s_na[16 * wave + 4 * quarter + e]);
+                    atomicAdd(&s_sum[2 * (d - 1)], (double)(gv[c][e] * ra * __builtin_amdgcn_rsqf(nb[c][e])));
+                    atomicAdd(&s_sum[2 * (d - 1) + 1], (double)(gd[c][e] * ra * __builtin_amdgcn_rsqf(nc[c][e])));
                 }
             }
         }
