@@ -39,6 +39,7 @@ namespace dsa {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -74,11 +75,59 @@ __device__ __forceinline__ float sum16(float v) {
 }
 
 // Each wavefront of a workgroup takes 16 consecutive queries (kMapWaves x 16
-// per workgroup); the 16-key tiles of K are staged in LDS once per
-// workgroup (coalesced 16-byte loads) and read by every wavefront.  Lane l
-// supplies tile row / column l % 16 and dimensions by l / 16 of each MFMA
-// step; it receives S[4 (l / 16) + e][l % 16], e = 0..3.
+// per workgroup); keys are staged in LDS kMapKeys at a time, once per
+// workgroup (coalesced 16-byte loads), and read by every wavefront as
+// 16-key MFMA tiles; the next stage is loaded into registers while the
+// current one is consumed.  Lane l supplies tile row / column l % 16 and
+// dimensions by l / 16 of each MFMA step; it receives S[4 (l / 16) + e][l %
+// 16], e = 0..3.
 constexpr int kMapWaves = 4;
+constexpr int kMapKeys = 64;  // keys per LDS stage: four 16-key tiles
+
+// One LDS stage of keys c0 .. c0 + kMapKeys - 1 of a lane (past the last key
+// of the group: repeats it; prompt keys first, then decode keys) held in
+// registers between its load and its store into LDS: 16-byte chunk x of the
+// stage (key x / RCH, part x % RCH) is thread x mod 256's entry x / 256.
+template <typename T, int D>
+struct KeyStage {
+    static constexpr int RCH = D * (int)sizeof(T) / 16;  // 16-byte chunks of a key row
+    static constexpr int PSTR = RCH + 1;                 // padded LDS row stride in chunks
+    static constexpr int NPF = kMapKeys * RCH / (64 * kMapWaves);
+    static_assert(kMapKeys * RCH % (64 * kMapWaves) == 0, "whole chunks per thread");
+    u32x4 v[NPF];  // a native vector type (HIP's uint4 is a union wrapper that kept the array in scratch)
+
+    __device__ __forceinline__ void load(const T* kp, const T* k, int L_p, int B, int H, int b, int h, int ncols,
+                                         int c0) {
+#pragma unroll
+        for (int n = 0; n < NPF; ++n) {
+            const int x = threadIdx.x + n * 64 * kMapWaves;
+            const int c = min(c0 + x / RCH, ncols - 1);
+            const T* prow = kp + (((size_t)b * L_p + min(c, max(L_p - 1, 0))) * H + h) * D;
+            const T* drow = k + (((size_t)max(c - L_p, 0) * B + b) * H + h) * D;
+            const T* krow = c < L_p ? prow : drow;
+            v[n] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(krow) + (x % RCH) * 16);
+        }
+    }
+    __device__ __forceinline__ void store(uint4* s_kt) const {
+        u32x4* dst = reinterpret_cast<u32x4*>(s_kt);
+#pragma unroll
+        for (int n = 0; n < NPF; ++n) {
+            const int x = threadIdx.x + n * 64 * kMapWaves;
+            dst[(x / RCH) * PSTR + x % RCH] = v[n];
+        }
+    }
+};
+
+// Logits of a wavefront's 16 queries (operand qa) against a staged 16-key
+// tile; krow: this lane's key row and dimension offset in LDS.
+template <typename T, int D>
+__device__ __forceinline__ f32x4 map_tile(const T* krow, const typename MfmaIn<T>::Op (&qa)[D / MfmaIn<T>::STEP]) {
+    using M = MfmaIn<T>;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < D / M::STEP; ++s) acc = M::mfma(qa[s], M::load(krow + s * M::STEP), acc);
+    return acc;
+}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs a) {
@@ -86,7 +135,6 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     constexpr int NS = D / M::STEP;
     constexpr int ROWB = D * (int)sizeof(T);        // bytes of a key row
     constexpr int RCH = ROWB / 16;                  // 16-byte chunks of a key row
-    constexpr int KCH = 16 * RCH;                   // ... of a 16-key tile
     constexpr int PSTR = RCH + 1;                   // padded LDS row stride in chunks: rows 16 B apart in banks
     const int tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
     const int lane = blockIdx.x / tiles;
@@ -98,7 +146,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     const T* q = reinterpret_cast<const T*>(a.q);
     const T* k = reinterpret_cast<const T*>(a.k);
     const T* kp = reinterpret_cast<const T*>(a.k_p);
-    __shared__ uint4 s_kt[16 * PSTR];  // the current 16-key tile, key-major
+    __shared__ uint4 s_kt[kMapKeys * PSTR];  // the current stage of keys, key-major
     const T* s_k = reinterpret_cast<const T*>(s_kt);
     // the query operand: row i0 + col (rows past T repeat T - 1 and are not stored)
     typename M::Op qa[NS];
@@ -108,24 +156,9 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         for (int s = 0; s < NS; ++s) qa[s] = M::load(qrow + s * M::STEP);
     }
     const int ncols = a.L_p + min((blockIdx.x % tiles) * 16 * kMapWaves + 16 * kMapWaves, a.T);  // keys of the group
-    auto stage = [&](int c0) {  // keys c0 .. c0 + 15 (past the last key: repeats it)
-        __syncthreads();
-        for (int x = threadIdx.x; x < KCH; x += 64 * kMapWaves) {
-            const int kk = x / RCH, part = x % RCH;
-            const int c = min(c0 + kk, ncols - 1);
-            const T* krow = c < a.L_p ? kp + (((size_t)b * a.L_p + c) * a.H + h) * D
-                                      : k + (((size_t)(c - a.L_p) * a.B + b) * a.H + h) * D;
-            s_kt[kk * PSTR + part] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(krow) + part * 16);
-        }
-        __syncthreads();
-    };
-    auto tile = [&]() {  // logits of the wavefront's 16 queries against the staged keys
-        const T* krow = s_k + col * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc = M::mfma(qa[s], M::load(krow + s * M::STEP), acc);
-        return acc;
-    };
+    // (the stage is used directly, not through lambdas: captured by
+    // reference, its registers would be demoted to scratch memory)
+    KeyStage<T, D> pf;
     const float scale = (float)(1.4426950408889634 / sqrt((double)D));  // log2(e) / sqrt(D)
 
     // pass 1: this lane's online (max, sum) per query over its columns, then
@@ -136,14 +169,21 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         m[e] = -INFINITY;
         s[e] = 0.0f;
     }
-    for (int c0 = 0; c0 < ncols; c0 += 16) {
-        stage(c0);
-        const int c = c0 + col;
-        const f32x4 t = tile();
+    pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
+    for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
+        __syncthreads();
+        pf.store(s_kt);
+        __syncthreads();
+        // unconditional (past the last key it rereads it): no merge of old and new registers
+        pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
+        for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
+            const int c = c0 + 16 * tt + col;
+            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter, qa);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = i0 + 4 * quarter + e;
-            if (c < ncols && c <= a.L_p + i) merge_ms(m[e], s[e], t[e] * scale, 1.0f);  // causal keys only
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + 4 * quarter + e;
+                if (c < ncols && c <= a.L_p + i) merge_ms(m[e], s[e], t[e] * scale, 1.0f);  // causal keys only
+            }
         }
     }
 #pragma unroll
@@ -158,21 +198,28 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     float inv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) inv[e] = 1.0f / s[e];
-    for (int c0 = 0; c0 < ncols; c0 += 16) {
-        stage(c0);
-        const int c = c0 + col;
-        const f32x4 t = tile();
-        const int j = c - a.L_p;  // decode position of the key
+    pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
+    for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
+        __syncthreads();
+        pf.store(s_kt);
+        __syncthreads();
+        // unconditional (past the last key it rereads it): no merge of old and new registers
+        pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
+        for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
+            const int c = c0 + 16 * tt + col;
+            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter, qa);
+            const int j = c - a.L_p;  // decode position of the key
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = i0 + 4 * quarter + e;
-            const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
-            const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
-            const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
-            mp[e] += j < 0 ? p : 0.0f;
-            ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
-            mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
-            if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + 4 * quarter + e;
+                const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
+                const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
+                const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
+                mp[e] += j < 0 ? p : 0.0f;
+                ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
+                mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
+                if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
+            }
         }
     }
 #pragma unroll
@@ -237,7 +284,12 @@ struct Staged {
 // wavefront: their rows, I0 + 64 g .. I0 + 64 g + 111, are staged once per
 // chunk for all four wavefronts (pass 0 holds the A rows among them; later
 // passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 x 17 floats.
-__global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileArgs a) {
+// MULTI: distances beyond one pass (max_dist > 16 kGramJ - 15): later passes
+// stage the A rows apart.  The one-pass form holds no registers for them and
+// fits three wavefronts per SIMD.
+template <bool MULTI>
+__global__ void __launch_bounds__(64 * kGramWaves) __attribute__((amdgpu_waves_per_eu(3)))
+profile_gram_kernel(ProfileArgs a) {
     // blockIdx -> (lane, row block) with all row blocks of a lane on one XCD
     // (workgroup x runs on XCD x % 8; lanes are padded to a multiple of 8):
     // they reread the lane's map from one L2.
@@ -264,12 +316,16 @@ __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileAr
 
     const int kend = min(I0 + 16 * kGramWaves, a.T);                 // P[i][k] = 0 for k > i
     const int span = 15 + a.max_dist;                                // columns i' - I needed: 0 .. span
-    const int passes = span / (16 * kGramJ) + 1;
+    const int passes = MULTI ? span / (16 * kGramJ) + 1 : 1;
     for (int g = 0; g < passes; ++g) {
         const int J0 = I + 16 * kGramJ * g;  // this wavefront's first column tile of the pass
         f32x4 gv[kGramJ], gd[kGramJ], nb[kGramJ], nc[kGramJ];
+        float sb[kGramJ], sc[kGramJ];  // sums of squares of the B rows over the chunks left of the tile
 #pragma unroll
-        for (int c = 0; c < kGramJ; ++c) gv[c] = gd[c] = nb[c] = nc[c] = f32x4{0, 0, 0, 0};
+        for (int c = 0; c < kGramJ; ++c) {
+            gv[c] = gd[c] = nb[c] = nc[c] = f32x4{0, 0, 0, 0};
+            sb[c] = sc[c] = 0.0f;
+        }
         const float* pA = g == 0 ? sPB : sPA;  // the A rows: inside the pass-0 B rows
         const float* qA = g == 0 ? sQB : sQA;
         const int aoff = 16 * wave;            // this wavefront's A rows in that buffer
@@ -278,17 +334,36 @@ __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileAr
         Staged<NB> nxB;
         Staged<16 * kGramWaves> nxA;
         nxB.load(P, a.T, I0 + 16 * kGramJ * g, 0);
-        if (g > 0) nxA.load(P, a.T, I0, 0);
+        if (MULTI && g > 0) nxA.load(P, a.T, I0, 0);
         for (int k0 = 0; k0 < kend; k0 += kGChunk) {
             __syncthreads();
             nxB.store(sPB, sQB);
-            if (g > 0) nxA.store(sPA, sQA);
+            if (MULTI && g > 0) nxA.store(sPA, sQA);
             __syncthreads();
             if (k0 + kGChunk < kend) {
                 nxB.load(P, a.T, I0 + 16 * kGramJ * g, k0 + kGChunk);
-                if (g > 0) nxA.load(P, a.T, I0, k0 + kGChunk);
+                if (MULTI && g > 0) nxA.load(P, a.T, I0, k0 + kGChunk);
             }
-            if (I < a.T) {
+            if (I < a.T && k0 + kGChunk - 1 < I) {
+                // every column of the chunk lies left of the tile's first row:
+                // L is 1 for all (i, k), so the prefix norms take plain sums
+                // of squares of the B rows (this lane: columns k = quarter mod 4)
+                for (int kk = 0; kk < kGChunk; kk += 4) {
+                    const int kl = kk + quarter;
+                    const float pa = pA[(aoff + col) * kGStride + kl];
+                    const float qa = qA[(aoff + col) * kGStride + kl];
+#pragma unroll
+                    for (int c = 0; c < kGramJ; ++c) {
+                        const int rb = 16 * (wave + c) + col;
+                        const float pb = sPB[rb * kGStride + kl];
+                        const float qb = sQB[rb * kGStride + kl];
+                        gv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, pb, gv[c], 0, 0, 0);
+                        gd[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, qb, gd[c], 0, 0, 0);
+                        sb[c] = fmaf(pb, pb, sb[c]);
+                        sc[c] = fmaf(qb, qb, sc[c]);
+                    }
+                }
+            } else if (I < a.T) {
                 const int kc = min(kGChunk, kend - k0);
                 for (int kk = 0; kk < kc; kk += 4) {
                     const int kl = kk + quarter;                               // this lane's column in the step
@@ -306,6 +381,20 @@ __global__ void __launch_bounds__(64 * kGramWaves) profile_gram_kernel(ProfileAr
                         nc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, qb * qb, nc[c], 0, 0, 0);
                     }
                 }
+            }
+        }
+        // the plain sums: over the four quarters of each column, added to
+        // every row of the tile
+#pragma unroll
+        for (int c = 0; c < kGramJ; ++c) {
+            float tb = sb[c] + __shfl_xor(sb[c], 16);
+            float tc = sc[c] + __shfl_xor(sc[c], 16);
+            tb += __shfl_xor(tb, 32);
+            tc += __shfl_xor(tc, 32);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nb[c][e] += tb;
+                nc[c][e] += tc;
             }
         }
         // lane holds entries (i, i') = (I + 4 quarter + e, J0 + 16 c + col)
@@ -386,8 +475,13 @@ hipError_t launch_profile_t(const ProfileArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const long long lanes8 = ((long long)a.lanes + 7) / 8 * 8;
     const int blocks = (tiles + kGramWaves - 1) / kGramWaves;
-    hipLaunchKernelGGL(profile_gram_kernel, dim3((unsigned)(lanes8 * blocks)), dim3(64 * kGramWaves),
-                       gram_lds_bytes(a.max_dist), s, a);
+    const bool multi = (15 + a.max_dist) / (16 * kGramJ) + 1 > 1;
+    if (multi)
+        hipLaunchKernelGGL(profile_gram_kernel<true>, dim3((unsigned)(lanes8 * blocks)), dim3(64 * kGramWaves),
+                           gram_lds_bytes(a.max_dist), s, a);
+    else
+        hipLaunchKernelGGL(profile_gram_kernel<false>, dim3((unsigned)(lanes8 * blocks)), dim3(64 * kGramWaves),
+                           gram_lds_bytes(a.max_dist), s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(profile_reduce_kernel, dim3((unsigned)a.lanes), dim3(64), 0, s, a);

@@ -78,6 +78,13 @@ def test_edge_cases(kw, max_dist):
     check_workload(tiny(**kw), max_dist)
 
 
+@pytest.mark.parametrize("T,max_dist", [(140, 49), (200, 120), (300, 256)])
+def test_distances_beyond_one_pass(T, max_dist):
+    """max_dist > 48: the similarity band spans several passes of four
+    column tiles (the multi-pass kernel form); 256 is the largest allowed."""
+    check_workload(tiny(L_dec=T, batch=1, heads=2), max_dist)
+
+
 def _as_inputs(q, kp, k, D):
     """fp32 lane arrays -> device tensors in the library layouts (one lane)."""
     T, d = q.shape
