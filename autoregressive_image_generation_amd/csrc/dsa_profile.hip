@@ -181,8 +181,18 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
             const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter, qa);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                // causal keys only; the running maximum moves only when a
+                // logit passes it by more than 8 (log2 units), so a key
+                // costs one exp2, and (m, s) stays exact for any m it holds
                 const int i = i0 + 4 * quarter + e;
-                if (c < ncols && c <= a.L_p + i) merge_ms(m[e], s[e], t[e] * scale, 1.0f);  // causal keys only
+                const bool ok = c < ncols && c <= a.L_p + i;
+                const float x = t[e] * scale;
+                const bool need = ok && !(x <= m[e] + 8.0f);
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    s[e] *= need ? __builtin_amdgcn_exp2f(m[e] - x) : 1.0f;
+                    m[e] = need ? x : m[e];
+                }
+                s[e] += ok ? __builtin_amdgcn_exp2f(x - m[e]) : 0.0f;
             }
         }
     }
