@@ -494,6 +494,10 @@ def characterize(w, inputs, dev, max_dist, reps=3):
     keys = T * L + T * (T + 1) // 2
     flops = 2.0 * D * keys * lanes
     map_bytes = 4.0 * (T * (T + 1) // 2) * lanes
+    # ... and of the similarities: the vertical and the diagonal dot products of
+    # every (i, i + d), i + 1 terms each (the prefix norms are running sums)
+    band = sum((T - d) * (T - d + 1) // 2 for d in range(1, max_dist + 1))
+    sim_flops = 2.0 * 2 * band * lanes
     picks = sorted({1, 2, w.grid_w, 2 * w.grid_w, max_dist} & set(range(1, max_dist + 1)))
     log("characterization: %.2f ms; mass prompt/local/middle %.3f/%.3f/%.3f" % (ms, *m))
     return {"layer": 0, "lanes": lanes, "T": T, "max_dist": max_dist, "ms": ms,
@@ -501,8 +505,9 @@ def characterize(w, inputs, dev, max_dist, reps=3):
             "vertical": {str(d): float(v[d - 1]) for d in picks},
             "diagonal": {str(d): float(g[d - 1]) for d in picks},
             "diagonal_minus_vertical_mean": float((g - v).mean()),
-            "map_flop": flops, "map_prob_bytes": map_bytes,
-            "note": "ms covers both kernels (map: MFMA logits + softmax, writes the fp32 map; similarity)"}
+            "map_flop": flops, "map_prob_bytes": map_bytes, "similarity_flop": sim_flops,
+            "note": "ms covers the three kernels (map: MFMA logits + softmax, writes the fp32 map; "
+                    "similarity: banded MFMA Gram products; per-lane means)"}
 
 
 def cpu_baseline(w, target_cpu_seconds):
