@@ -122,6 +122,15 @@ int check_state(const dsa_state* st, int kind, int kind2 = -1) {
 
 // Score-policy (TOVA / H2O) sizes: [0] free slot, [4 + j] slot positions, in
 // 16-byte chunks; the H2O logits of one lane live in LDS next to them.
+// MXFP8 states: clear the cache rows on the state's stream, so that every
+// row the kernel reads holds zeros or codes the quantiser wrote (finite
+// values, scale bytes below 0xFF), including rows no token has reached yet.
+int clear_mx_rows(dsa_state* st, size_t kv_region_bytes) {
+    if (st->dtype != DSA_MXFP8) return DSA_OK;
+    hipError_t e = hipMemsetAsync(st->ws, 0, kv_region_bytes, st->stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "MXFP8 cache clear");
+}
+
 int meta_stride_for(int N_att) { return (4 + N_att + 3) / 4 * 4; }
 int score_stride_for(int N_att) { return (N_att + 1) / 2 * 2; }
 constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
@@ -345,6 +354,11 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->ring_off = (size_t)st->lanes * (size_t)L_p * row_bytes(head_dim, dtype);
     st->list_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
     st->stream = static_cast<hipStream_t>(hip_stream);
+    rc = clear_mx_rows(st, st->list_off);
+    if (rc) {
+        delete st;
+        return rc;
+    }
     *out = st;
     return DSA_OK;
 }
@@ -396,6 +410,11 @@ int dsa_policy_state_init(dsa_state** out, int policy, int batch, int L_p, int N
     st->score_off = st->meta_off + align_up((size_t)st->lanes * (size_t)st->meta_stride * sizeof(int32_t));
     st->n_recent = policy == DSA_POLICY_H2O ? N_r : 0;
     st->stream = static_cast<hipStream_t>(hip_stream);
+    rc = clear_mx_rows(st, st->meta_off);
+    if (rc) {
+        delete st;
+        return rc;
+    }
     *out = st;
     return DSA_OK;
 }
@@ -539,6 +558,11 @@ int dense_state_init(dsa_state** out, int batch, int L_p, int L_max, int heads, 
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
     st->stream = static_cast<hipStream_t>(hip_stream);
+    rc = clear_mx_rows(st, kv_bytes(st->lanes, st->lane_rows, head_dim, dtype));
+    if (rc) {
+        delete st;
+        return rc;
+    }
     *out = st;
     return DSA_OK;
 }

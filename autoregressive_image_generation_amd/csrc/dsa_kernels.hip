@@ -429,15 +429,15 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                 if (valid && d == kSelfOutOfStream && sl == 0) s_self_j = max(jj, 0);
             }
             valid = valid && d != kSelfOutOfStream;
-            // a row that does not count may be an unwritten cache row (the
-            // current token's placeholder): zero its bytes so that no NaN code
-            // reaches the accumulator through a zero weight
-            const uint32_t keep = valid ? 0xffffffffu : 0u;
-            unpack_e4m3(make_uint4(ch.k.x & keep, ch.k.y & keep, ch.k.z & keep, ch.k.w & keep), kf);
-            unpack_e4m3(make_uint4(ch.v.x & keep, ch.v.y & keep, ch.v.z & keep, ch.v.w & keep), vf);
+            // A row that does not count (the current token's placeholder, a
+            // row past the group's share) enters with weight 0.  Every cache
+            // row holds zeros (cleared at state init) or the quantiser's codes
+            // (no NaN code, scale bytes below 0xFF), so 0 times its values is 0.
+            unpack_e4m3(ch.k, kf);
+            unpack_e4m3(ch.v, vf);
             const int b = sl * EPT / 32;  // this thread's elements lie in block b of 32
-            kscale = (double)e8m0_value((ch.s.x & keep) >> (8 * b) & 0xffu);
-            vscale = e8m0_value((ch.s.y & keep) >> (8 * b) & 0xffu);
+            kscale = (double)e8m0_value(ch.s.x >> (8 * b) & 0xffu);
+            vscale = e8m0_value(ch.s.y >> (8 * b) & 0xffu);
         } else {
             unpack<T>(ch.k, kf);
             unpack<T>(ch.v, vf);

@@ -70,6 +70,9 @@ typedef enum {
  * attended in its quantised form, the current token's included.  The pages
  * call KV quantization stackable with the selection (Section 6) and fix no
  * format.  A row then takes 2 * head_dim + 8 bytes instead of 4 * head_dim.
+ * The *_init calls of DSA_MXFP8 states clear the workspace's cache rows on
+ * the state's stream (hipMemsetAsync), so whatever the workspace held before
+ * never reaches the attention; the other dtypes enqueue nothing at init.
  */
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_MXFP8 = 2 } dsa_dtype;
 

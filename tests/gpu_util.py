@@ -33,21 +33,28 @@ def device_inputs(w, layer, T, dev):
     return q, k, v, kp, vp
 
 
-def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None):
+def _workspace(nbytes, dev, fill):
+    if fill is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return torch.full((nbytes,), fill, dtype=torch.uint8, device=dev)
+
+
+def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, fill=None):
     """T steps of one layer.  Returns out [T][B][H][D] (device), trace [T][B][H][2]
     (host) and, with read_every > 0, {t: (offsets, counts)} read after step t.
-    With `policy` the state comes from dsa_policy_state_init (N_r defaults to w.N_r)."""
+    With `policy` the state comes from dsa_policy_state_init (N_r defaults to w.N_r).
+    `fill`: a byte the workspace holds before init (default: whatever it held)."""
     q, k, v, kp, vp = inputs
     B, H, D = w.batch, w.heads, w.head_dim
     stream = torch.cuda.current_stream(dev)
     if policy is None:
         nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = _workspace(nbytes, dev, fill)
         st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes, stream)
     else:
         n_r = w.N_r if N_r is None else N_r
         nbytes = dsa.dsa_policy_workspace_bytes(policy, B, w.L_p, n_r, w.N_att, H, D, w.dtype)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = _workspace(nbytes, dev, fill)
         st = dsa.dsa_policy_state_init(policy, B, w.L_p, n_r, w.N_att, H, D, w.dtype, ws, nbytes, stream)
     dsa.dsa_set_waves(st, waves)
     out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
@@ -70,11 +77,11 @@ def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None):
     return out, trace.cpu().numpy(), reads
 
 
-def run_dense(w, inputs, T, dev, waves=0):
+def run_dense(w, inputs, T, dev, waves=0, fill=None):
     q, k, v, kp, vp = inputs
     B, H, D = w.batch, w.heads, w.head_dim
     nbytes = dsa.dense_state_workspace_bytes(B, w.L_p, T, H, D, w.dtype)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws = _workspace(nbytes, dev, fill)
     st = dsa.dense_state_init(B, w.L_p, T, H, D, w.dtype, ws, nbytes, torch.cuda.current_stream(dev))
     dsa.dsa_set_waves(st, waves)
     out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)

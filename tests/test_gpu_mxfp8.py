@@ -41,12 +41,12 @@ def bf16(x):
     return oracle.widen(x, synth.BF16)
 
 
-def _parity(w, waves=0, read_every=0, layer=0, lanes=None):
-    say("mxfp8 parity %s T=%d N_r=%d N_att=%d sink=%d d=%d waves=%d" % (
-        w.name, w.L_dec, w.N_r, w.N_att, w.sink, w.head_dim, waves))
+def _parity(w, waves=0, read_every=0, layer=0, lanes=None, fill=None):
+    say("mxfp8 parity %s T=%d N_r=%d N_att=%d sink=%d d=%d waves=%d fill=%s" % (
+        w.name, w.L_dec, w.N_r, w.N_att, w.sink, w.head_dim, waves, fill))
     T = w.L_dec
     ins = device_inputs(w, layer, T, DEV)
-    out, trace, _ = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every)
+    out, trace, _ = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, fill=fill)
     lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
     stats = {}
     for (b, h) in lanes:
@@ -127,11 +127,20 @@ def test_edge_cases(kw):
     _parity(tiny(**kw))
 
 
-def test_dense_matches_oracle_on_quantised_kv():
+@pytest.mark.parametrize("kw", [dict(), dict(sink=4, head_dim=128), dict(N_r=64, N_att=64)])
+def test_workspace_garbage_never_reaches_the_attention(kw):
+    """The workspace starts as 0xFF bytes (NaN codes, an infinite scale byte):
+    the cache clear at init keeps every row the kernel reads finite, also the
+    rows no token has reached and the current token's own slot."""
+    _parity(tiny(**kw), fill=0xFF)
+
+
+@pytest.mark.parametrize("fill", [None, 0xFF])
+def test_dense_matches_oracle_on_quantised_kv(fill):
     w = tiny(head_dim=128, batch=2)
     T = w.L_dec
     ins = device_inputs(w, 0, T, DEV)
-    out = run_dense(w, ins, T, DEV).cpu().numpy()
+    out = run_dense(w, ins, T, DEV, fill=fill).cpu().numpy()
     err = 0.0
     for b in range(w.batch):
         for h in range(w.heads):
@@ -142,10 +151,11 @@ def test_dense_matches_oracle_on_quantised_kv():
 
 @pytest.mark.parametrize("policy", [dsa.DSA_POLICY_SLIDING_WINDOW, dsa.DSA_POLICY_STREAMING_LLM,
                                     dsa.DSA_POLICY_TOVA, dsa.DSA_POLICY_H2O])
-def test_policies_on_quantised_kv(policy):
+@pytest.mark.parametrize("fill", [None, 0xFF])
+def test_policies_on_quantised_kv(policy, fill):
     from test_gpu_policies import check_policy
 
-    _, stats = check_policy(policy, tiny(head_dim=128, batch=2), read_every=4)
+    _, stats = check_policy(policy, tiny(head_dim=128, batch=2), read_every=4, fill=fill)
     assert stats["max_err"] <= MX_TOL
 
 
