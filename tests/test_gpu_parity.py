@@ -93,6 +93,18 @@ def test_edge_cases(kw):
     _parity(tiny(**kw), read_every=3)
 
 
+def test_largest_attended_list():
+    """N_att - sink = DSA_MAX_ATTEND (8192 window offsets staged in LDS, 1024
+    16-byte chunks loaded in the kernel's loop past the first two rounds):
+    phase 1 through t = 8190, the selections at t = 8191 .. 8198, then phase
+    3, on both lanes in lockstep with the oracle, for one-wavefront and
+    sixteen-wavefront workgroups."""
+    w = tiny(batch=1, heads=2, L_p=4, N_r=8200, N_att=8192, L_dec=8201)
+    for waves in (1, 16):
+        _, _, stats = _parity(w, waves=waves)
+        assert stats["selections"] == 2 * 8
+
+
 def test_deterministic_across_runs():
     w = tiny(dtype=synth.BF16, head_dim=128, batch=2)
     ins = device_inputs(w, 0, w.L_dec, DEV)

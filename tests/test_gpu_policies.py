@@ -202,3 +202,11 @@ def test_janus_pro_7b_shape_sampled_lanes(policy):
             col = flat[:, lane]
             col = col[col >= 0]
             assert len(np.unique(col)) == len(col)
+
+
+def test_h2o_largest_cache():
+    """L_p + N_att = DSA_MAX_H2O_ROWS (4096 fp64 logits of a lane in LDS): the
+    cache fills, then evicts on every step, in lockstep with the oracle."""
+    w = synth.WORKLOADS["tiny_fp32"].with_(batch=1, heads=2, L_p=96, N_att=4000, N_r=2000, L_dec=4010)
+    _, stats = check_policy(dsa.DSA_POLICY_H2O, w)
+    assert stats["choices"] == 2 * 11
