@@ -120,8 +120,6 @@ int check_state(const dsa_state* st, int kind, int kind2 = -1) {
     return 0;
 }
 
-// Score-policy (TOVA / H2O) sizes: [0] free slot, [4 + j] slot positions, in
-// 16-byte chunks; the H2O logits of one lane live in LDS next to them.
 // MXFP8 states: clear the cache rows on the state's stream, so that every
 // row the kernel reads holds zeros or codes the quantiser wrote (finite
 // values, scale bytes below 0xFF), including rows no token has reached yet.
@@ -131,6 +129,8 @@ int clear_mx_rows(dsa_state* st, size_t kv_region_bytes) {
     return e == hipSuccess ? DSA_OK : hip_fail(e, "MXFP8 cache clear");
 }
 
+// Score-policy (TOVA / H2O) sizes: [0] free slot, [4 + j] slot positions, in
+// 16-byte chunks; the H2O logits of one lane live in LDS next to them.
 int meta_stride_for(int N_att) { return (4 + N_att + 3) / 4 * 4; }
 int score_stride_for(int N_att) { return (N_att + 1) / 2 * 2; }
 constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
