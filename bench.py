@@ -8,9 +8,14 @@ The default workload is the Janus-Pro-7B shape (batch 96, 30 layers, 32 heads x
 128, L_p 64, L_dec 576 on a 24x24 grid, N_r 288, N_att 29 = 95 % sparsity).
 
 Printed: one JSON line with head-steps/s (batch x layers x heads x L_dec per
-second) and HBM GB/s, the dense kernel at batch 32 beside it, the roofline of
-the sparse kernel from per-launch HIP events, and the CPU oracle on a bounded
-sample of the same workload.
+second) and HBM GB/s of the decode split into two micro-batch streams; the
+roofline of the sparse kernel (the same decode on one stream, whole batch per
+launch, from HIP events on the launch stream) and of the two-stream aggregate;
+the dense kernel at batch 32 beside the sparse one at the same batch; the
+sparse-KV baselines at the same budget (SlidingWindow, StreamingLLM, TOVA,
+H2O); the MXFP8 cache; the attention-map characterization of one layer; the
+device's HBM read ceiling from a plain read probe; and the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
