@@ -726,7 +726,11 @@ def main():
                            "ms_per_step": dsec * 1e3, "sparse_same_batch_value": dsteps / ssec,
                            "sparse_speedup": dsec / ssec,
                            "byte_ratio": dbytes / (sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec))
-                                                   * db * w.heads * layers)}
+                                                   * db * w.heads * layers),
+                           # the headline sparse decode (full batch) against the dense kernel at
+                           # this batch, per head-step, next to (L_p + N_r) / (L_p + N_att)
+                           "sparse_headline_vs_dense": (head_steps / sec) / (dsteps / dsec),
+                           "budget_ratio": (w.L_p + w.N_r) / (w.L_p + w.N_att)}
         log("dense b%d: %.1f ms per decode; sparse b%d %.1f ms -> %.2fx" % (db, dsec * 1e3, db, ssec * 1e3,
                                                                            dsec / ssec))
         del dense, sparse_b
