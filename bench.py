@@ -591,8 +591,8 @@ def main():
         summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (lanes shard across GPUs "
-              "with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: no multi-GPU path is implemented (lanes would shard across "
+              "GPUs with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
