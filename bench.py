@@ -460,6 +460,29 @@ def hbm_read_ceiling(dev, nbytes=4 << 30, reps=10):
     return best
 
 
+def launch_floor(dev, blocks, threads, n=5000):
+    """Average duration of back-to-back launches, on one stream, of a near-empty
+    kernel with the decode launch's grid (the read probe over 16 bytes per
+    thread): the per-launch cost any dependent kernel of that shape pays here."""
+    import torch
+
+    import autoregressive_image_generation_amd as dsa
+
+    nbytes = blocks * threads * 16
+    src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(100):
+        dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, stream)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, stream)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    return start.elapsed_time(stop) * 1e3 / n
+
+
 def characterize(w, inputs, dev, max_dist, reps=3):
     """Section 3.4 measurements (Figs. 8 and 10) on the dense decode map of
     layer 0, all lanes: mean mass split and vertical / diagonal similarity,
@@ -654,6 +677,19 @@ def main():
     bytes_per_launch = total_bytes / n_launch
     achieved = bytes_per_launch / launch_s / 1e9
     log("sparse kernel alone: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
+    # the per-launch floor of a kernel with the same grid: the library's
+    # wavefront rule for one stream (whole batch per launch) fixes the block
+    lanes = w.batch * w.heads
+    wv = args.waves
+    if not wv:
+        ept = 4 if w.dtype == synth.F32 else 8
+        gpw = 64 // (w.head_dim // ept)
+        rows = w.L_p + w.N_att
+        wv = 1
+        while wv < 8 and lanes * 2 * wv < 3072 and rows >= 4 * gpw * 2 * wv:
+            wv *= 2
+    floor_us = launch_floor(dev, lanes, 64 * wv)
+    log("launch floor (near-empty kernel, %d x %d threads): %.2f us" % (lanes, 64 * wv, floor_us))
     # per-phase latency from one decode with an event pair around every launch
     # (each pair adds ~2 us of event overhead; for the step profile only)
     durs = kernel_durations(single, layers, dev)
@@ -698,6 +734,8 @@ def main():
                      "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
                      "avg_launch_us": launch_s * 1e6,
                      "bytes_per_launch": bytes_per_launch,
+                     "launch_floor_us": floor_us,
+                     "achieved_above_floor": bytes_per_launch / (launch_s - floor_us * 1e-6) / 1e9,
                      "event_pair_us_by_phase": phase_us,
                      "event_pair_us_by_step": step_series},
         "events_ms_per_step": sec_ev * 1e3,
