@@ -460,10 +460,12 @@ def hbm_read_ceiling(dev, nbytes=4 << 30, reps=10):
     return best
 
 
-def launch_floor(dev, blocks, threads, n=5000):
-    """Average duration of back-to-back launches, on one stream, of a near-empty
-    kernel with the decode launch's grid (the read probe over 16 bytes per
-    thread): the per-launch cost any dependent kernel of that shape pays here."""
+def launch_floor(dev, blocks, threads, nodes=48, reps=40):
+    """Device time per launch of a near-empty kernel with the decode launch's
+    grid (the read probe over 16 bytes per thread), back to back on one
+    stream.  The launches are replayed from a captured graph: issued one by one
+    from Python they would be bound by the host (~3.5 us per call), not by the
+    device.  What any dependent kernel of that shape pays per launch here."""
     import torch
 
     import autoregressive_image_generation_amd as dsa
@@ -471,16 +473,29 @@ def launch_floor(dev, blocks, threads, n=5000):
     nbytes = blocks * threads * 16
     src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(100):
-        dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, stream)
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, side)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(nodes):
+            dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, torch.cuda.current_stream(dev))
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize(dev)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
     start.record(stream)
-    for _ in range(n):
-        dsa.dsa_hbm_read_probe(src, nbytes, blocks, threads, 1, sink, stream)
+    for _ in range(reps):
+        graph.replay()
     stop.record(stream)
     torch.cuda.synchronize(dev)
-    return start.elapsed_time(stop) * 1e3 / n
+    us = start.elapsed_time(stop) * 1e3 / (reps * nodes)
+    if int(sink.item()) != 0:
+        raise RuntimeError("read probe: the sink was written for a zero buffer")
+    del graph
+    return us
 
 
 def characterize(w, inputs, dev, max_dist, reps=3):
@@ -689,7 +704,7 @@ def main():
         while wv < 8 and lanes * 2 * wv < 3072 and rows >= 4 * gpw * 2 * wv:
             wv *= 2
     floor_us = launch_floor(dev, lanes, 64 * wv)
-    log("launch floor (near-empty kernel, %d x %d threads): %.2f us" % (lanes, 64 * wv, floor_us))
+    log("launch floor (near-empty kernel, %d x %d threads, graph replay): %.2f us" % (lanes, 64 * wv, floor_us))
     # per-phase latency from one decode with an event pair around every launch
     # (each pair adds ~2 us of event overhead; for the step profile only)
     durs = kernel_durations(single, layers, dev)
