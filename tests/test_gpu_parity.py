@@ -114,6 +114,26 @@ def test_deterministic_across_runs():
     np.testing.assert_array_equal(t1, t2)
 
 
+@pytest.mark.parametrize("waves", [1, 4])
+def test_lanes_are_independent(waves):
+    """Selections are per head (Section 4): permuting the batch and the heads of
+    every input permutes the outputs and the traces the same way, bit for bit."""
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=3, heads=4)
+    T = w.L_dec
+    q, k, v, kp, vp = device_inputs(w, 0, T, DEV)
+    o1, t1, _ = run_sparse(w, (q, k, v, kp, vp), T, DEV, waves=waves)
+    pb = torch.tensor([2, 0, 1], device=DEV)
+    ph = torch.tensor([3, 1, 0, 2], device=DEV)
+
+    def perm(x, bdim, hdim):
+        return x.index_select(bdim, pb).index_select(hdim, ph).contiguous()
+
+    ins = (perm(q, 1, 2), perm(k, 1, 2), perm(v, 1, 2), perm(kp, 0, 2), perm(vp, 0, 2))
+    o2, t2, _ = run_sparse(w, ins, T, DEV, waves=waves)
+    assert torch.equal(o2, perm(o1, 1, 2))
+    np.testing.assert_array_equal(t2, t1[:, [2, 0, 1]][:, :, [3, 1, 0, 2]])
+
+
 def test_append_decode_step_matches_the_two_calls():
     w = tiny(dtype=synth.BF16, head_dim=128, batch=2)
     T = w.L_dec
