@@ -373,7 +373,7 @@ profile_gram_kernel(ProfileArgs a) {
                         sc[c] = fmaf(qb, qb, sc[c]);
                     }
                 }
-            } else if (I < a.T) {
+            } else if (I < a.T && k0 <= I + 15) {  // past I + 15 this wavefront's A rows are zero
                 const int kc = min(kGChunk, kend - k0);
                 for (int kk = 0; kk < kc; kk += 4) {
                     const int kl = kk + quarter;                               // this lane's column in the step
