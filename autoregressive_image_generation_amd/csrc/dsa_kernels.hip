@@ -224,12 +224,12 @@ __device__ __forceinline__ double wave_sum(double v) {
 // position for window entries, -1 for prompt and sink rows).
 constexpr int kSelfOutOfStream = -2;
 
-// EARLY: every thread group's first U rows need no list or slot entry (U * G
-// <= number of prompt + sink rows), so they are requested before the lane's
-// index data has arrived.
+// NE: how many of every thread group's first U rows are requested before the
+// lane's index data has arrived (rows g + u * G with u < NE need no list or
+// slot entry: NE * G <= number of prompt + sink rows).
 // MXFP8 holds 16 elements per thread and needs more than 128 VGPRs, so its
 // workgroups stop at 8 wavefronts.
-template <typename F, int D, int MODE, int U, bool EARLY>
+template <typename F, int D, int MODE, int U, int NE>
 __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a) {
     using T = typename F::In;
     constexpr bool MX = F::MX;
@@ -240,6 +240,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     constexpr bool SLOTS = MODE == MODE_TOVA || MODE == MODE_H2O;
     constexpr int IEPT = 16 / (int)sizeof(T);     // input elements per 16-byte chunk
     constexpr int CH = 2 * D / IEPT;              // 16-byte chunks of an input K|V row
+    static_assert(CH <= 64, "the lanes of wave 0 hold the appended row");
 
     // Dynamic LDS: the lane's index data, staged once per launch.  Sparse: the
     // attended window offsets (int16).  TOVA / H2O: the slot metadata (int32:
@@ -279,7 +280,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
 
     // Requests in the order their data is needed: the index data (16-byte
     // chunks; strides are padded to whole chunks), the query chunk, the
-    // appended row, then (EARLY) the first prompt rows.  Vector loads complete
+    // appended row, then (NE > 0) the first prompt rows.  Vector loads complete
     // in issue order, so waiting for the index data only waits for what was
     // issued before it.
     const int nch = MODE == MODE_SPARSE ? (a.n_list + 7) / 8 : SLOTS ? (a.n_meta + 3) / 4 : 0;
@@ -370,15 +371,17 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
 
     typename F::Chunk cx[U];
     int dd[U];
-    auto first_rows = [&]() {
+    // the group's first rows u in [u0, u1) (constants at both call sites)
+    auto first_rows = [&](int u0, int u1) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (u < u0 || u >= u1) continue;
             const char *kr, *vr, *sr;
             row_src(min(g + u * G, R - 1), kr, vr, sr, dd[u]);
             cx[u] = load_row(kr, vr, sr);
         }
     };
-    if constexpr (EARLY) first_rows();  // prompt rows only: no index data read
+    if constexpr (NE > 0) first_rows(0, NE);  // prompt rows only: no index data read
     if constexpr (MODE != MODE_DENSE) {
         if constexpr (MX && MODE == MODE_SPARSE) {
             if (tid == 0) s_self_j = -1;
@@ -392,7 +395,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         // free slot: clamped like the offsets above
         if (a.free_host < 0) fslot = min(max(s_meta[0], 0), a.N_cache - 1);
     }
-    if constexpr (!EARLY) first_rows();
+    if constexpr (NE < U) first_rows(NE, U);
 
     double qd[EPT];
     {
@@ -506,8 +509,10 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     // Append: the new K/V row goes to its cache row.  Nothing this launch
     // reads lives there (it is empty, holds the entry evicted at this step, or
     // is the free slot); the current token itself is read from k_new / v_new
-    // (plain) or from the registers below (MXFP8).  Loaded at the start,
-    // stored here, so it adds no latency of its own.
+    // (plain) or from the registers below (MXFP8).  Loaded at the start and
+    // stored by wave 0 after its last global load: loads and stores share one
+    // counter whose wait cannot tell them apart, so a store issued before a
+    // load would make the wait for that load also wait for the store.
     char* dst_row;
     if constexpr (MODE == MODE_SPARSE)
         dst_row = const_cast<char*>(ring) + ((size_t)a.self_row * a.lanes + lane) * RB;
@@ -515,6 +520,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         dst_row = const_cast<char*>(lane_kv) + (size_t)(a.L_p + (SLOTS ? fslot : a.self_row)) * RB;
     uint2 qcode = make_uint2(0, 0);  // MXFP8: this lane's 8 codes of the new row (lanes < CH of wave 0)
     uint32_t qscale = 0;             // and the E8M0 scale of its block
+    uint32_t qw0 = 0, qw1 = 0;       // the row's scale word: K block b at byte b, V block b at byte 4 + b
     if constexpr (MX) {
         if (wave == 0) {
             // lanes 0 .. CH/2-1 hold K, CH/2 .. CH-1 hold V, 8 elements each;
@@ -530,22 +536,24 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             for (int e = 0; e < 8; ++e) c[e] = e4m3_rne_sat(ldexpf(xf[e], -X));
             qcode = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
             qscale = (uint32_t)(X + 127);
-            // the scale word: K block b at byte b, V block b at byte 4 + b
-            uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int b = 0; b < D / 32; ++b) {
-                w0 |= (uint32_t)__shfl((int)qscale, 4 * b) << (8 * b);
-                w1 |= (uint32_t)__shfl((int)qscale, CH / 2 + 4 * b) << (8 * b);
+                qw0 |= (uint32_t)__shfl((int)qscale, 4 * b) << (8 * b);
+                qw1 |= (uint32_t)__shfl((int)qscale, CH / 2 + 4 * b) << (8 * b);
             }
+        }
+    }
+    auto store_append = [&]() {
+        if constexpr (MX) {
             if (tid < CH) {
                 const int off = tid < CH / 2 ? 8 * tid : D + 8 * (tid - CH / 2);
                 *reinterpret_cast<uint2*>(dst_row + off) = qcode;
             }
-            if (tid == 0) *reinterpret_cast<uint2*>(dst_row + 2 * D) = make_uint2(w0, w1);
+            if (tid == 0) *reinterpret_cast<uint2*>(dst_row + 2 * D) = make_uint2(qw0, qw1);
+        } else {
+            if (tid < CH) *reinterpret_cast<uint4*>(dst_row + tid * 16) = ax;
         }
-    } else {
-        if (tid < CH) *reinterpret_cast<uint4*>(dst_row + tid * 16) = ax;
-    }
+    };
 
     // Merge the groups of this wavefront (butterfly over lanes TPR apart).
 #pragma unroll
@@ -636,12 +644,20 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                 sm.m = mn;
             }
         }
-        const float inv = 1.0f / sm.l;
-        float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4)
-            o4[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
     }
+    // The output and the appended row are stored once no global load is left
+    // (H2O: after its score update).
+    auto store_results = [&]() {
+        if (wl < TPR) {
+            const float inv = 1.0f / sm.l;
+            float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
+#pragma unroll
+            for (int e = 0; e < EPT; e += 4)
+                o4[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+        }
+        store_append();
+    };
+    if constexpr (MODE != MODE_H2O) store_results();
 
     if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
         if (wl != 0) return;
@@ -745,6 +761,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                 a.trace[2 * lane + 1] = -1;
             }
         }
+        store_results();
     }
 }
 
@@ -821,6 +838,18 @@ __global__ void prompt_kernel(PromptArgs a) {
     }
 }
 
+template <typename F, int D, int U, int MODE>
+void launch_decode_m(int G, int win0, dim3 grid, dim3 block, size_t lds, const DecodeArgs& a, hipStream_t s) {
+    // rows per group that need no index data: all U, one, or none
+    const int ne = win0 / G;
+    if (ne >= U)
+        hipLaunchKernelGGL((decode_kernel<F, D, MODE, U, U>), grid, block, lds, s, a);
+    else if (ne >= 1)
+        hipLaunchKernelGGL((decode_kernel<F, D, MODE, U, 1>), grid, block, lds, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<F, D, MODE, U, 0>), grid, block, lds, s, a);
+}
+
 template <typename F, int D, int U>
 hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
     constexpr int TPR = D / F::EPT;
@@ -829,31 +858,19 @@ hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t
     switch (mode) {
         case MODE_SPARSE: {
             const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;
-            if (U * G <= a.L_p + a.n_sink)
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_SPARSE, U, true>), grid, block, lds, s, a);
-            else
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_SPARSE, U, false>), grid, block, lds, s, a);
+            launch_decode_m<F, D, U, MODE_SPARSE>(G, a.L_p + a.n_sink, grid, block, lds, a, s);
             break;
         }
         case MODE_DENSE:
-            hipLaunchKernelGGL((decode_kernel<F, D, MODE_DENSE, U, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<F, D, MODE_DENSE, U, U>), grid, block, 0, s, a);
             break;
-        case MODE_TOVA: {
-            const size_t lds = (size_t)a.meta_stride * 4;
-            if (U * G <= a.L_p)
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_TOVA, U, true>), grid, block, lds, s, a);
-            else
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_TOVA, U, false>), grid, block, lds, s, a);
+        case MODE_TOVA:
+            launch_decode_m<F, D, U, MODE_TOVA>(G, a.L_p, grid, block, (size_t)a.meta_stride * 4, a, s);
             break;
-        }
-        default: {  // MODE_H2O: slot metadata, then one fp64 logit per attended row
-            const size_t lds = (size_t)a.meta_stride * 4 + (size_t)(a.L_p + a.N_cache) * 8;
-            if (U * G <= a.L_p)
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_H2O, U, true>), grid, block, lds, s, a);
-            else
-                hipLaunchKernelGGL((decode_kernel<F, D, MODE_H2O, U, false>), grid, block, lds, s, a);
+        default:  // MODE_H2O: slot metadata, then one fp64 logit per attended row
+            launch_decode_m<F, D, U, MODE_H2O>(G, a.L_p, grid, block,
+                                               (size_t)a.meta_stride * 4 + (size_t)(a.L_p + a.N_cache) * 8, a, s);
             break;
-        }
     }
     return hipGetLastError();
 }
