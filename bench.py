@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC = {
     # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
     # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.77e6, "kernel_sha256_16": "22673cf34ad842ef"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.77e6, "kernel_sha256_16": "79e579d093eaf27b"},
     # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.47e6, "kernel_sha256_16": "22673cf34ad842ef"},
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.47e6, "kernel_sha256_16": "79e579d093eaf27b"},
     # MXFP8 cache, two micro-batches of 48: dispatches 24000-24599 of its own decode kernel
     # (steps 400-409), algorithmic 39.39 MB; its 264-byte rows straddle 64-byte segments
-    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.93e6, "kernel_sha256_16": "22673cf34ad842ef"},
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.94e6, "kernel_sha256_16": "79e579d093eaf27b"},
 }
 
 
