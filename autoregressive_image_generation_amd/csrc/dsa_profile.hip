@@ -40,6 +40,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -91,7 +92,9 @@ constexpr int kMapKeys = 64;  // keys per LDS stage: four 16-key tiles
 template <typename T, int D>
 struct KeyStage {
     static constexpr int RCH = D * (int)sizeof(T) / 16;  // 16-byte chunks of a key row
-    static constexpr int PSTR = RCH + 1;                 // padded LDS row stride in chunks
+    // LDS row stride in 8-byte units: a key row plus 8 bytes, so that the 16
+    // rows of an MFMA operand read start in different banks
+    static constexpr int RSTR = 2 * RCH + 1;
     static constexpr int NPF = kMapKeys * RCH / (64 * kMapWaves);
     static_assert(kMapKeys * RCH % (64 * kMapWaves) == 0, "whole chunks per thread");
     u32x4 v[NPF];  // a native vector type (HIP's uint4 is a union wrapper that kept the array in scratch)
@@ -108,12 +111,13 @@ struct KeyStage {
             v[n] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(krow) + (x % RCH) * 16);
         }
     }
-    __device__ __forceinline__ void store(uint4* s_kt) const {
-        u32x4* dst = reinterpret_cast<u32x4*>(s_kt);
+    __device__ __forceinline__ void store(u32x2* s_kt) const {
 #pragma unroll
         for (int n = 0; n < NPF; ++n) {
             const int x = threadIdx.x + n * 64 * kMapWaves;
-            dst[(x / RCH) * PSTR + x % RCH] = v[n];
+            u32x2* dst = s_kt + (x / RCH) * RSTR + 2 * (x % RCH);  // 8-byte aligned: two stores
+            dst[0] = v[n].xy;
+            dst[1] = v[n].zw;
         }
     }
 };
@@ -133,9 +137,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs a) {
     using M = MfmaIn<T>;
     constexpr int NS = D / M::STEP;
-    constexpr int ROWB = D * (int)sizeof(T);        // bytes of a key row
-    constexpr int RCH = ROWB / 16;                  // 16-byte chunks of a key row
-    constexpr int PSTR = RCH + 1;                   // padded LDS row stride in chunks: rows 16 B apart in banks
+    constexpr int RSTR = KeyStage<T, D>::RSTR;      // LDS row stride in 8-byte units
     const int tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
     const int lane = blockIdx.x / tiles;
     const int wave = threadIdx.x / 64;
@@ -146,7 +148,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     const T* q = reinterpret_cast<const T*>(a.q);
     const T* k = reinterpret_cast<const T*>(a.k);
     const T* kp = reinterpret_cast<const T*>(a.k_p);
-    __shared__ uint4 s_kt[kMapKeys * PSTR];  // the current stage of keys, key-major
+    __shared__ u32x2 s_kt[kMapKeys * RSTR];  // the current stage of keys, key-major
     const T* s_k = reinterpret_cast<const T*>(s_kt);
     // the query operand: row i0 + col (rows past T repeat T - 1 and are not stored)
     typename M::Op qa[NS];
@@ -178,7 +180,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
         for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
             const int c = c0 + 16 * tt + col;
-            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter, qa);
+            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // causal keys only; the running maximum moves only when a
@@ -217,7 +219,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
         for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
             const int c = c0 + 16 * tt + col;
-            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (PSTR * 16 / (int)sizeof(T)) + M::PER * quarter, qa);
+            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
             const int j = c - a.L_p;  // decode position of the key
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
