@@ -23,11 +23,16 @@
 // with L[i][k] = 1 for k <= i (P[i][k] = 0 beyond k = i).  A workgroup of
 // four wavefronts takes 64 rows; each wavefront computes the 16 x 16 tiles
 // of the four products for its 16 rows and the columns i + 1 .. i +
-// max_dist with MFMA (v_mfma_f32_16x16x4_f32), four column tiles per pass,
-// from 16-column chunks of the rows staged once for all four wavefronts in
-// LDS (padded stride: no bank conflicts; the next chunk is loaded into
-// registers while the current one is consumed), and adds each cosine into
-// per-distance sums.
+// max_dist, four column tiles per pass, from 16-column chunks of the rows
+// staged once for all four wavefronts in LDS (padded strides: no bank
+// conflicts; the next chunk is loaded into registers while the current one
+// is consumed), and adds each cosine into per-distance sums.  The two Gram
+// products take each value split into two bf16 parts (hi = bf16(x), lo =
+// bf16(x - hi), so x = hi + lo + r with |r| <= 2^-18 |x|) and sum hi.hi +
+// hi.lo + lo.hi with bf16 MFMA (v_mfma_f32_16x16x16_bf16, one step per
+// 16-column chunk): every partial product is exact in fp32, and each term
+// x y is missed by less than 2^-16 |x y| (the dropped lo.lo and r terms).  The norms stay in fp32 (plain sums of squares left of a tile,
+// v_mfma_f32_16x16x4_f32 with L across it).
 // profile_reduce_kernel: per lane, the sums over row tiles in order, the
 // means, and the mean mass split.
 #include <math.h>
@@ -251,6 +256,16 @@ constexpr int kGramWaves = 4;  // row tiles per workgroup (one per wavefront)
 constexpr int kGramJ = 4;      // column tiles per pass (accumulators: 4 products x 4 tiles)
 constexpr int kGChunk = 16;    // staged columns per LDS chunk (its prefetch registers still fit 3 waves per SIMD)
 constexpr int kGStride = kGChunk + 1;
+// bf16 row stride of the split copies: 40 bytes, so that the 16 rows of an
+// MFMA operand read (8 bytes each) start in different banks
+constexpr int kGBStride = 20;
+
+// The staged rows in LDS: fp32 (for the norms) and split into bf16 hi / lo
+// (for the Gram products), for P and for Q.
+struct GStage {
+    float *p, *q;
+    uint16_t *ph, *pl, *qh, *ql;
+};
 
 // Columns [k0, k0 + kGChunk) of NROWS rows r0.. of the map, as P (row-major,
 // zero beyond the causal part and past T) and as Q (offset coordinates:
@@ -281,12 +296,24 @@ struct Staged {
             pq += (size_t)RSTEP * (T + 1);
         }
     }
-    __device__ __forceinline__ void store(float* sP, float* sQ) const {
+    __device__ __forceinline__ void store(const GStage& st) const {
         const int off = (threadIdx.x / kGChunk) * kGStride + threadIdx.x % kGChunk;
+        const int boff = (threadIdx.x / kGChunk) * kGBStride + threadIdx.x % kGChunk;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            sP[off + n * RSTEP * kGStride] = p[n];
-            sQ[off + n * RSTEP * kGStride] = q[n];
+            st.p[off + n * RSTEP * kGStride] = p[n];
+            st.q[off + n * RSTEP * kGStride] = q[n];
+            // p and q split together: two packed conversions (round to nearest even)
+            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+            const bf16x2v h2 = {(__bf16)p[n], (__bf16)q[n]};
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h2);
+            const bf16x2v l2 = {(__bf16)(p[n] - __uint_as_float(hb << 16)),
+                                (__bf16)(q[n] - __uint_as_float(hb & 0xffff0000u))};
+            const uint32_t lb = __builtin_bit_cast(uint32_t, l2);
+            st.ph[boff + n * RSTEP * kGBStride] = (uint16_t)hb;
+            st.qh[boff + n * RSTEP * kGBStride] = (uint16_t)(hb >> 16);
+            st.pl[boff + n * RSTEP * kGBStride] = (uint16_t)lb;
+            st.ql[boff + n * RSTEP * kGBStride] = (uint16_t)(lb >> 16);
         }
     }
 };
@@ -322,6 +349,11 @@ profile_gram_kernel(ProfileArgs a) {
     float* sQB = sPB + NB * kGStride;
     float* sPA = sQB + NB * kGStride;  // later passes only
     float* sQA = sPA + 16 * kGramWaves * kGStride;
+    constexpr int NA = MULTI ? 16 * kGramWaves : 0;
+    uint16_t* hb = reinterpret_cast<uint16_t*>(s_dyn + 2 * (NB + NA) * kGStride);  // 8-byte aligned
+    const GStage stB{sPB, sQB, hb, hb + NB * kGBStride, hb + 2 * NB * kGBStride, hb + 3 * NB * kGBStride};
+    uint16_t* ha = hb + 4 * NB * kGBStride;
+    const GStage stA{sPA, sQA, ha, ha + NA * kGBStride, ha + 2 * NA * kGBStride, ha + 3 * NA * kGBStride};
     __shared__ double s_sum[2 * kMaxProfileDist];  // per distance: vertical, diagonal
     __shared__ float s_na[16 * kGramWaves];        // |P[i][0..i]|^2 of the block's rows
     for (int d = threadIdx.x; d < 2 * a.max_dist; d += 64 * kGramWaves) s_sum[d] = 0.0;
@@ -338,9 +370,33 @@ profile_gram_kernel(ProfileArgs a) {
             gv[c] = gd[c] = nb[c] = nc[c] = f32x4{0, 0, 0, 0};
             sb[c] = sc[c] = 0.0f;
         }
-        const float* pA = g == 0 ? sPB : sPA;  // the A rows: inside the pass-0 B rows
-        const float* qA = g == 0 ? sQB : sQA;
         const int aoff = 16 * wave;            // this wavefront's A rows in that buffer
+        const GStage& sa = g == 0 ? stB : stA;
+        // The chunk's Gram products, all 16 columns in one step per product:
+        // bf16 MFMA (16 x 16 x 16) of the split operands, hi.hi + hi.lo + lo.hi.
+        // Lane l holds columns 4 (l / 16) .. + 3 of row l % 16 of A and of B.
+        auto gram_chunk = [&]() {
+            typedef short bf16x4v __attribute__((ext_vector_type(4)));
+            const int ao = (aoff + col) * kGBStride + 4 * quarter;
+            const bf16x4v pah = *reinterpret_cast<const bf16x4v*>(sa.ph + ao);
+            const bf16x4v pal = *reinterpret_cast<const bf16x4v*>(sa.pl + ao);
+            const bf16x4v qah = *reinterpret_cast<const bf16x4v*>(sa.qh + ao);
+            const bf16x4v qal = *reinterpret_cast<const bf16x4v*>(sa.ql + ao);
+#pragma unroll
+            for (int c = 0; c < kGramJ; ++c) {
+                const int bo = (16 * (wave + c) + col) * kGBStride + 4 * quarter;
+                const bf16x4v pbh = *reinterpret_cast<const bf16x4v*>(stB.ph + bo);
+                const bf16x4v pbl = *reinterpret_cast<const bf16x4v*>(stB.pl + bo);
+                const bf16x4v qbh = *reinterpret_cast<const bf16x4v*>(stB.qh + bo);
+                const bf16x4v qbl = *reinterpret_cast<const bf16x4v*>(stB.ql + bo);
+                gv[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, pbh, gv[c], 0, 0, 0);
+                gd[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qah, qbh, gd[c], 0, 0, 0);
+                gv[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, pbl, gv[c], 0, 0, 0);
+                gd[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qah, qbl, gd[c], 0, 0, 0);
+                gv[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, pbh, gv[c], 0, 0, 0);
+                gd[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qal, qbh, gd[c], 0, 0, 0);
+            }
+        };
         // the next chunk's rows are loaded into registers while this one is
         // consumed from LDS
         Staged<NB> nxB;
@@ -349,8 +405,8 @@ profile_gram_kernel(ProfileArgs a) {
         if (MULTI && g > 0) nxA.load(P, a.T, I0, 0);
         for (int k0 = 0; k0 < kend; k0 += kGChunk) {
             __syncthreads();
-            nxB.store(sPB, sQB);
-            if (MULTI && g > 0) nxA.store(sPA, sQA);
+            nxB.store(stB);
+            if (MULTI && g > 0) nxA.store(stA);
             __syncthreads();
             if (k0 + kGChunk < kend) {
                 nxB.load(P, a.T, I0 + 16 * kGramJ * g, k0 + kGChunk);
@@ -360,35 +416,31 @@ profile_gram_kernel(ProfileArgs a) {
                 // every column of the chunk lies left of the tile's first row:
                 // L is 1 for all (i, k), so the prefix norms take plain sums
                 // of squares of the B rows (this lane: columns k = quarter mod 4)
+                gram_chunk();
                 for (int kk = 0; kk < kGChunk; kk += 4) {
                     const int kl = kk + quarter;
-                    const float pa = pA[(aoff + col) * kGStride + kl];
-                    const float qa = qA[(aoff + col) * kGStride + kl];
 #pragma unroll
                     for (int c = 0; c < kGramJ; ++c) {
                         const int rb = 16 * (wave + c) + col;
                         const float pb = sPB[rb * kGStride + kl];
                         const float qb = sQB[rb * kGStride + kl];
-                        gv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, pb, gv[c], 0, 0, 0);
-                        gd[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, qb, gd[c], 0, 0, 0);
                         sb[c] = fmaf(pb, pb, sb[c]);
                         sc[c] = fmaf(qb, qb, sc[c]);
                     }
                 }
             } else if (I < a.T && k0 <= I + 15) {  // past I + 15 this wavefront's A rows are zero
+                // A rows are zero past column I + 15, so the Gram step may
+                // run over all 16 columns
+                gram_chunk();
                 const int kc = min(kGChunk, kend - k0);
                 for (int kk = 0; kk < kc; kk += 4) {
                     const int kl = kk + quarter;                               // this lane's column in the step
-                    const float pa = pA[(aoff + col) * kGStride + kl];          // A[row = col][k]
-                    const float qa = qA[(aoff + col) * kGStride + kl];
                     const float ind = (k0 + kl <= I + col) ? 1.0f : 0.0f;       // L[I + col][k]
 #pragma unroll
                     for (int c = 0; c < kGramJ; ++c) {
                         const int rb = 16 * (wave + c) + col;                   // B row J0 + 16 c + col
                         const float pb = sPB[rb * kGStride + kl];
                         const float qb = sQB[rb * kGStride + kl];
-                        gv[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, pb, gv[c], 0, 0, 0);
-                        gd[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa, qb, gd[c], 0, 0, 0);
                         nb[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, pb * pb, nb[c], 0, 0, 0);
                         nc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, qb * qb, nc[c], 0, 0, 0);
                     }
@@ -444,7 +496,7 @@ profile_gram_kernel(ProfileArgs a) {
 size_t gram_lds_bytes(int max_dist) {
     const int passes = (15 + max_dist) / (16 * kGramJ) + 1;
     const int rows = 16 * (kGramWaves + kGramJ - 1) + (passes > 1 ? 16 * kGramWaves : 0);
-    return (size_t)rows * 2 * kGStride * sizeof(float);
+    return (size_t)rows * (2 * kGStride * sizeof(float) + 4 * kGBStride * sizeof(uint16_t));
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
