@@ -37,6 +37,7 @@ from .binding import (
     dsa_read_state,
     dsa_set_stream,
     dsa_set_waves,
+    dsa_set_splits,
     dsa_state_destroy,
     dsa_state_init,
     dsa_state_step,

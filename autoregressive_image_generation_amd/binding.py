@@ -43,6 +43,7 @@ _SIGNATURES = {
     "dsa_attention_profile": (_c_int, [_P, _P, _P] + [_c_int] * 7 + [_P, _c_size, _P, _P, _P, _P]),
     "dsa_hbm_read_probe": (_c_int, [_P, _c_size, _c_int, _c_int, _c_int, _P, _P]),
     "dsa_set_waves": (_c_int, [_P, _c_int]),
+    "dsa_set_splits": (_c_int, [_P, _c_int]),
     "dsa_state_step": (_c_int, [_P]),
     "dsa_state_destroy": (_c_int, [_P]),
     "dsa_strerror": (ctypes.c_char_p, [_c_int]),
@@ -235,6 +236,10 @@ def dsa_hbm_read_probe(src, nbytes, blocks, threads, unroll, sink, stream=None):
 
 def dsa_set_waves(st, waves_per_lane):
     return _check(library().dsa_set_waves(st, waves_per_lane))
+
+
+def dsa_set_splits(st, splits_per_lane):
+    return _check(library().dsa_set_splits(st, splits_per_lane))
 
 
 def dsa_state_step(st) -> int:

@@ -56,6 +56,9 @@ struct dsa_state {
     const void* pend_k;
     const void* pend_v;
     int waves;
+    int splits;               // sparse: workgroups per lane requested (0 = the library's choice)
+    size_t part_off, ctr_off;  // sparse: split records and per-lane arrival counters
+    int counters_clear;       // sparse: the counters were zeroed (before the first split launch)
     // SCORE states: per-lane slot metadata and (H2O) accumulated scores
     size_t meta_off, score_off;
     int meta_stride, score_stride, n_recent;
@@ -103,6 +106,12 @@ size_t kv_bytes(long long lanes, long long lane_rows, int D, int dtype) {
     return align_up((size_t)lanes * (size_t)lane_rows * row_bytes(D, dtype));
 }
 
+// Sparse states: the records of split launches (up to kMaxSplits per lane).
+size_t split_rec_bytes(long long lanes, int D) {
+    return align_up((size_t)lanes * dsa::kMaxSplits * dsa::split_rec_floats(D) * sizeof(float));
+}
+size_t counter_bytes(long long lanes) { return align_up((size_t)lanes * sizeof(int32_t)); }
+
 int check_workspace(void* ws, size_t have, size_t need) {
     if (!ws) return fail(DSA_E_WORKSPACE, "workspace pointer is NULL");
     if ((uintptr_t)ws % kAlign) return fail(DSA_E_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
@@ -140,14 +149,23 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // lane), so waves doubles while lanes * waves stays below 3072, every thread
 // group keeps at least the pipeline depth (4 rows) of work, and the workgroup
 // stays at 8 wavefronts or fewer (16 was slower at every measured shape).
-int choose_waves(const dsa_state* st, long long rows) {
+int choose_waves(const dsa_state* st, long long rows, int splits = 1) {
     const int max_w = st->dtype == DSA_MXFP8 ? 8 : 16;  // MXFP8 workgroups stop at 8 wavefronts
     if (st->waves) return std::min(st->waves, max_w);
     const int ept = st->dtype == DSA_F32 ? 4 : st->dtype == DSA_MXFP8 ? 16 : 8;  // elements per thread
     const int gpw = 64 / (st->D / ept);
+    const long long wgs = (long long)st->lanes * splits;  // workgroups per launch
+    const long long per = (rows + splits - 1) / splits;   // rows per workgroup
     int w = 1;
-    while (w < 8 && (long long)st->lanes * (2 * w) < 3072 && rows >= 4ll * gpw * (2 * w)) w *= 2;
+    while (w < 8 && wgs * (2 * w) < 3072 && per >= 4ll * gpw * (2 * w)) w *= 2;
     return w;
+}
+
+// Workgroups per lane of a sparse launch: the state's request, or 1.  Only
+// plain-row (bf16 / fp32) sparse states split.
+int choose_splits(const dsa_state* st) {
+    if (st->kind != KIND_SPARSE || st->dtype == DSA_MXFP8) return 1;
+    return st->splits ? st->splits : 1;
 }
 
 int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
@@ -163,6 +181,7 @@ int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
         a.v_p = v_p;
         a.kv = st->ws;
         a.list = init_list ? reinterpret_cast<int16_t*>(st->ws + st->list_off) : nullptr;
+        a.counter = nullptr;
         a.lane_rows = st->lane_rows;
         a.B = st->batch;
         a.H = st->heads;
@@ -208,6 +227,7 @@ void fill_common(const dsa_state* st, const void* q_t, float* out, dsa::DecodeAr
     a.L_p = st->L_p;
     a.t = st->t;
     a.scale_log2e = 1.4426950408889634 / sqrt((double)st->D);
+    a.splits = 1;
 }
 
 // Map a dsa_policy onto a state kind.  Diagonal (with or without sinks)
@@ -320,7 +340,8 @@ size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int hea
     if (check_sparse(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype)) return 0;
     const long long lanes = (long long)batch * heads;
     return kv_bytes(lanes, (long long)L_p + N_r, head_dim, dtype) +
-           align_up((size_t)lanes * (size_t)list_stride_for(N_att - sink) * sizeof(int16_t));
+           align_up((size_t)lanes * (size_t)list_stride_for(N_att - sink) * sizeof(int16_t)) +
+           split_rec_bytes(lanes, head_dim) + counter_bytes(lanes);
 }
 
 int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
@@ -353,6 +374,8 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->ws_bytes = workspace_bytes;
     st->ring_off = (size_t)st->lanes * (size_t)L_p * row_bytes(head_dim, dtype);
     st->list_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
+    st->part_off = st->list_off + align_up((size_t)st->lanes * (size_t)st->list_stride * sizeof(int16_t));
+    st->ctr_off = st->part_off + split_rec_bytes(st->lanes, head_dim);
     st->stream = static_cast<hipStream_t>(hip_stream);
     rc = clear_mx_rows(st, st->list_off);
     if (rc) {
@@ -467,7 +490,24 @@ int dsa_decode_step(dsa_state* st, const void* q_t, float* out, int32_t* trace) 
     // Phase 3 (t >= N_r): the oldest non-sink entry t - (N_r - S) leaves.
     a.evicted = t >= st->N_r ? t - N_rw : -1;
 
-    const int waves = choose_waves(st, (long long)st->L_p + S + N_attw);
+    const int splits = choose_splits(st);
+    if (splits > 1 && !st->counters_clear) {
+        // arrivals counted from zero; a fill kernel (the prompt kernel with
+        // nothing to copy), not a memset, so the step stays capturable
+        dsa::PromptArgs pa;
+        memset(&pa, 0, sizeof(pa));
+        pa.kv = st->ws;
+        pa.counter = reinterpret_cast<int32_t*>(st->ws + st->ctr_off);
+        pa.B = st->batch;
+        pa.H = st->heads;
+        hipError_t e = dsa::launch_prompt(st->dtype, st->D, pa, st->stream);
+        if (e != hipSuccess) return hip_fail(e, "split counter clear");
+        st->counters_clear = 1;
+    }
+    a.splits = splits;
+    a.partial = reinterpret_cast<float*>(st->ws + st->part_off);
+    a.counter = reinterpret_cast<int32_t*>(st->ws + st->ctr_off);
+    const int waves = choose_waves(st, (long long)st->L_p + S + N_attw, splits);
     hipError_t e = dsa::launch_decode(dsa::MODE_SPARSE, st->dtype, st->D, waves, a, st->stream);
     if (e != hipSuccess) return hip_fail(e, "sparse decode launch");
     st->pend_k = st->pend_v = nullptr;
@@ -679,6 +719,18 @@ int dsa_set_waves(dsa_state* st, int waves_per_lane) {
         waves_per_lane != 8 && waves_per_lane != 16)
         return fail(DSA_E_INVAL, "waves_per_lane must be 0, 1, 2, 4, 8 or 16 (got %d)", waves_per_lane);
     st->waves = waves_per_lane;
+    return DSA_OK;
+}
+
+int dsa_set_splits(dsa_state* st, int splits_per_lane) {
+    int rc = check_state(st, 0);
+    if (rc) return rc;
+    if (splits_per_lane != 0 && splits_per_lane != 1 && splits_per_lane != 2 && splits_per_lane != 4)
+        return fail(DSA_E_INVAL, "splits_per_lane must be 0, 1, 2 or 4 (got %d)", splits_per_lane);
+    if (splits_per_lane > 1 && (st->kind != KIND_SPARSE || st->dtype == DSA_MXFP8))
+        return fail(DSA_E_INVAL, "only sparse states with bf16 or fp32 rows split (got a %s state, dtype %d)",
+                    kind_name(st->kind), st->dtype);
+    st->splits = splits_per_lane;
     return DSA_OK;
 }
 

@@ -58,13 +58,24 @@ struct DecodeArgs {
     int free_host;         // slot of the current token when the host knows it (t < N_cache), else -1
     int n_recent;          // H2O: protected most recent positions
     double inv_sqrt_d;     // H2O: 1 / sqrt(D), for the fp64 probabilities
+    // Split launches (sparse, plain rows; 1 otherwise): `splits` workgroups per
+    // lane, each over a contiguous slice of the lane's rows.
+    int splits;
+    float* partial;        // [lanes][splits] records of split_rec_floats(D) floats
+    int32_t* counter;      // [lanes] arrivals of the current launch; 0 between launches
 };
+
+// A split's partial state: acc[D], m, l, the argmin candidate's fp64 logit,
+// its offset and its list index, padded to 16 bytes.
+constexpr int split_rec_floats(int D) { return D + 8; }
+constexpr int kMaxSplits = 4;
 
 struct PromptArgs {
     const void* k_p;       // [B][L_p][H][D]
     const void* v_p;
     void* kv;
     int16_t* list;         // nullable: when set, list[lane * list_stride] = 0 for every lane
+    int32_t* counter;      // nullable: when set, counter[lane] = 0 for every lane
     long long lane_rows;
     int B, H, L_p, list_stride;
 };

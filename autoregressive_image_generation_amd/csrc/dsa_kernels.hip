@@ -229,7 +229,8 @@ constexpr int kSelfOutOfStream = -2;
 // slot entry: NE * G <= number of prompt + sink rows).
 // MXFP8 holds 16 elements per thread and needs more than 128 VGPRs, so its
 // workgroups stop at 8 wavefronts.
-template <typename F, int D, int MODE, int U, int NE>
+// SPLIT: a split launch (a.splits workgroups per lane; sparse, plain rows).
+template <typename F, int D, int MODE, int U, int NE, bool SPLIT = false>
 __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a) {
     using T = typename F::In;
     constexpr bool MX = F::MX;
@@ -256,7 +257,13 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     __shared__ int s_bd[kMaxWaves], s_bj[kMaxWaves];
     __shared__ int s_self_j;  // MXFP8 sparse: list index of the current token, -1 if not attended
 
-    const int lane = blockIdx.x;
+    // Split launches (sparse, plain rows): workgroup x takes a contiguous
+    // slice of the rows of lane x / splits, and the last of the lane's
+    // workgroups to finish combines their partial states.
+    static_assert(!SPLIT || (MODE == MODE_SPARSE && !MX && NE == 0), "split launches: sparse, plain rows");
+    const int nsplit = SPLIT ? a.splits : 1;
+    const int lane = SPLIT ? (int)blockIdx.x / nsplit : (int)blockIdx.x;
+    const int split = SPLIT ? (int)blockIdx.x % nsplit : 0;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int wl = tid & 63;
@@ -277,6 +284,9 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                   : MODE == MODE_DENSE ? a.L_p + a.t + 1
                                        : a.L_p + a.n_occ + 1;
     const int win0 = MODE == MODE_SPARSE ? a.L_p + a.n_sink : MODE == MODE_DENSE ? R : a.L_p;
+    // this workgroup's rows [r0, r1) (all of them unless split)
+    const int per = (R + nsplit - 1) / nsplit;
+    const int r0 = min(R, split * per), r1 = min(R, r0 + per);
 
     // Requests in the order their data is needed: the index data (16-byte
     // chunks; strides are padded to whole chunks), the query chunk, the
@@ -366,8 +376,8 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     // Rows of this group: r_k = g + k * G.  Every group of a wavefront runs the
     // trip count of the wavefront's first group; rows past R re-read row R-1
     // (cached) and are not consumed.
-    const int nk = (R - g + G - 1) / G;                      // rows this group consumes
-    const int nkw = (R - wave * GPW + G - 1) / G;             // trip count of the wavefront
+    const int nk = (r1 - r0 - g + G - 1) / G;                // rows this group consumes
+    const int nkw = (r1 - r0 - wave * GPW + G - 1) / G;       // trip count of the wavefront
 
     typename F::Chunk cx[U];
     int dd[U];
@@ -377,7 +387,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         for (int u = 0; u < U; ++u) {
             if (u < u0 || u >= u1) continue;
             const char *kr, *vr, *sr;
-            row_src(min(g + u * G, R - 1), kr, vr, sr, dd[u]);
+            row_src(min(r0 + g + u * G, r1 - 1), kr, vr, sr, dd[u]);
             cx[u] = load_row(kr, vr, sr);
         }
     };
@@ -418,7 +428,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     // of MXFP8, enter with logit -inf and weight 0: selects instead of
     // branches, so the loop below stays straight-line.
     auto consume = [&](int k, const typename F::Chunk& ch, int d) {
-        const int r = g + k * G;
+        const int r = r0 + g + k * G;
         int jj = r - win0;  // sparse: list index; TOVA: the slot (below)
         if constexpr (MODE == MODE_TOVA) jj = jj == a.n_occ ? fslot : jj + (jj >= fslot ? 1 : 0);
         float kf[EPT], vf[EPT];
@@ -499,7 +509,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         for (int u = 0; u < U; ++u) {
             consume(k0 + u, cx[u], dd[u]);
             const char *kr, *vr, *sr;
-            row_src(min(g + (k0 + u + U) * G, R - 1), kr, vr, sr, dd[u]);
+            row_src(min(r0 + g + (k0 + u + U) * G, r1 - 1), kr, vr, sr, dd[u]);
             cx[u] = load_row(kr, vr, sr);
         }
     }
@@ -645,6 +655,80 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             }
         }
     }
+    if constexpr (SPLIT) {
+        {
+            // This workgroup's partial state: (m, l, acc) and its argmin
+            // candidate over all its wavefronts, as one record.
+#pragma unroll 1
+            for (int w = 1; w < nwaves; ++w) {
+                if (s_bd[w] >= 0 && (best_d < 0 || better(s_bs[w], s_bd[w], best_s, best_d))) {
+                    best_s = s_bs[w];
+                    best_d = s_bd[w];
+                    best_j = s_bj[w];
+                }
+            }
+            // The record goes out with device-coherent stores (written through
+            // to the point where the XCDs meet), and the arrival counter is a
+            // device-scope atomic issued after those stores have completed; the
+            // last workgroup reads the records back the same coherent way.  No
+            // cache-wide write-back or invalidate is needed.
+            float* rec = a.partial + (size_t)blockIdx.x * split_rec_floats(D);
+            if (wl < TPR) {
+#pragma unroll
+                for (int e = 0; e < EPT; ++e)
+                    __hip_atomic_store(rec + sl * EPT + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (wl == 0) {
+                __hip_atomic_store(rec + D, sm.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(rec + D + 1, sm.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<double*>(rec + D + 2), best_s, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<int*>(rec) + D + 4, best_d, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<int*>(rec) + D + 5, best_j, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_s_waitcnt(0);            // the record's stores have completed
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // and the compiler keeps them first
+            int arrived = 0;
+            if (wl == 0)
+                arrived = __hip_atomic_fetch_add(a.counter + lane, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arrived = __shfl(arrived, 0);
+            if (arrived != nsplit - 1) return;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (wl == 0) __hip_atomic_store(a.counter + lane, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the records merged in split order (the argmin order is total)
+            sm = Softmax{kNegBig, 0.0f};
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) acc[e] = 0.0f;
+            best_s = __builtin_inf();
+            best_d = best_j = -1;
+            for (int s2 = 0; s2 < nsplit; ++s2) {
+                float* r2 = a.partial + ((size_t)lane * nsplit + s2) * split_rec_floats(D);
+                if (wl < TPR) {
+                    float acc2[EPT];
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e)
+                        acc2[e] = __hip_atomic_load(r2 + sl * EPT + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float m2 = __hip_atomic_load(r2 + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float l2 = __hip_atomic_load(r2 + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    merge<EPT>(sm, acc, m2, l2, acc2);
+                }
+                const double bs2 =
+                    __hip_atomic_load(reinterpret_cast<double*>(r2 + D + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int bd2 =
+                    __hip_atomic_load(reinterpret_cast<int*>(r2) + D + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int bj2 =
+                    __hip_atomic_load(reinterpret_cast<int*>(r2) + D + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (bd2 >= 0 && (best_d < 0 || better(bs2, bd2, best_s, best_d))) {
+                    best_s = bs2;
+                    best_d = bd2;
+                    best_j = bj2;
+                }
+            }
+        }
+    }
+
     // The output and the appended row are stored once no global load is left
     // (H2O: after its score update).
     auto store_results = [&]() {
@@ -831,15 +915,25 @@ __global__ void prompt_kernel(PromptArgs a) {
             *reinterpret_cast<uint4*>(dst) = load16(src);
         }
     }
-    if (a.list) {
+    if (a.list || a.counter) {
         const int lanes = a.B * a.H;
-        for (int l = blockIdx.x * blockDim.x + threadIdx.x; l < lanes; l += gridDim.x * blockDim.x)
-            a.list[(size_t)l * a.list_stride] = 0;
+        for (int l = blockIdx.x * blockDim.x + threadIdx.x; l < lanes; l += gridDim.x * blockDim.x) {
+            if (a.list) a.list[(size_t)l * a.list_stride] = 0;
+            if (a.counter) a.counter[l] = 0;
+        }
     }
 }
 
 template <typename F, int D, int U, int MODE>
 void launch_decode_m(int G, int win0, dim3 grid, dim3 block, size_t lds, const DecodeArgs& a, hipStream_t s) {
+    if constexpr (MODE == MODE_SPARSE && !F::MX) {
+        // split launches issue no row before the index list: a slice past the
+        // first may start inside the window
+        if (a.splits > 1) {
+            hipLaunchKernelGGL((decode_kernel<F, D, MODE, U, 0, true>), grid, block, lds, s, a);
+            return;
+        }
+    }
     // rows per group that need no index data: all U, one, or none
     const int ne = win0 / G;
     if (ne >= U)
@@ -854,7 +948,7 @@ template <typename F, int D, int U>
 hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
     constexpr int TPR = D / F::EPT;
     const int G = waves * (64 / TPR);
-    dim3 grid(a.lanes), block(64 * waves);
+    dim3 grid(a.lanes * a.splits), block(64 * waves);
     switch (mode) {
         case MODE_SPARSE: {
             const size_t lds = (size_t)((a.n_list + 7) / 8 > 0 ? (a.n_list + 7) / 8 : 1) * 16;

@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC = {
     # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
     # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.77e6, "kernel_sha256_16": "79e579d093eaf27b"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.77e6, "kernel_sha256_16": "10acee0bdd10da79"},
     # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.47e6, "kernel_sha256_16": "79e579d093eaf27b"},
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.47e6, "kernel_sha256_16": "10acee0bdd10da79"},
     # MXFP8 cache, two micro-batches of 48: dispatches 24000-24599 of its own decode kernel
     # (steps 400-409), algorithmic 39.39 MB; its 264-byte rows straddle 64-byte segments
-    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.94e6, "kernel_sha256_16": "79e579d093eaf27b"},
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.94e6, "kernel_sha256_16": "10acee0bdd10da79"},
 }
 
 
@@ -224,7 +224,7 @@ class SparseModel:
     independent, so one's launch can overlap another's.
     """
 
-    def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1, policy=None):
+    def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1, policy=None, splits=0):
         import torch
 
         import autoregressive_image_generation_amd as dsa
@@ -247,6 +247,7 @@ class SparseModel:
         self.out = torch.empty((self.B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
         self.streams = [torch.cuda.current_stream(dev)] if streams == 1 else micro_batch_streams(dev, streams)
         self.waves = waves
+        self.splits = splits
         self.states = []  # [micro-batch][layer]
 
     def _init_state(self, ws, stream):
@@ -278,6 +279,7 @@ class SparseModel:
             for layer, ws in enumerate(self.ws[c]):
                 st = self._init_state(ws, self.streams[c])
                 dsa.dsa_set_waves(st, self.waves)
+                dsa.dsa_set_splits(st, getattr(self, "splits", 0))
                 self._append_prompt(st, self.inputs.layers[layer], c)
                 row.append(st)
             self.states.append(row)

@@ -83,8 +83,10 @@ typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_MXFP8 = 2 } dsa_dtype;
  * Device workspace bytes of a sparse state: per lane a cache of L_p prompt
  * rows plus an N_r-entry ring of decode rows (each row K then V, head_dim
  * elements each), which is the footprint bound N_r + L_p of Section 4 "Cost
- * analysis", plus the per-lane list of attended window offsets.  Returns 0
- * when the parameters are invalid (same rules as dsa_state_init).
+ * analysis", plus the per-lane list of attended window offsets, plus the
+ * records of split launches (dsa_set_splits: up to 4 records of
+ * 4 * (head_dim + 8) bytes per lane, and one arrival counter per lane).
+ * Returns 0 when the parameters are invalid (same rules as dsa_state_init).
  */
 size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int heads, int head_dim, int sink,
                                  int dtype);
@@ -232,6 +234,25 @@ int dense_append_decode_step(dsa_state* st, const void* k_t, const void* v_t, co
  * the softmax sums.
  */
 int dsa_set_waves(dsa_state* st, int waves_per_lane);
+
+/*
+ * Workgroups per lane of a sparse state's decode launches: 1, 2 or 4, or 0
+ * for the library's choice.  With n > 1, workgroup s of a lane takes the
+ * s-th of n contiguous slices of the lane's attended rows (prompt, sinks,
+ * window entries) and leaves its partial softmax state (m, l, acc) and argmin
+ * candidate in the workspace; the last of the lane's workgroups to finish
+ * (a per-lane arrival counter; no workgroup waits) merges the n records in
+ * slice order and performs the output, the state update and the append.  This
+ * is the split combine of a lane's attention (the pages fuse the whole step
+ * into one kernel, Section 5.1).  Choices, evictions and offsets do not depend
+ * on n (the argmin order is total); outputs only through fp32 rounding order.
+ * Only states with bf16 or fp32 rows split: DSA_MXFP8 and the dense, TOVA and
+ * H2O states accept 0 or 1.  The first split launch of a state is preceded
+ * by a small kernel that zeroes the counters; every split launch leaves them
+ * at zero.  Two launches of one state must not overlap (they share the
+ * counters), which the state's single stream ensures.
+ */
+int dsa_set_splits(dsa_state* st, int splits_per_lane);
 
 /*
  * Attention-map characterization (Section 3.4 of the pages: Fig. 8, attention

@@ -39,11 +39,12 @@ def _workspace(nbytes, dev, fill):
     return torch.full((nbytes,), fill, dtype=torch.uint8, device=dev)
 
 
-def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, fill=None):
+def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, fill=None, splits=0):
     """T steps of one layer.  Returns out [T][B][H][D] (device), trace [T][B][H][2]
     (host) and, with read_every > 0, {t: (offsets, counts)} read after step t.
     With `policy` the state comes from dsa_policy_state_init (N_r defaults to w.N_r).
-    `fill`: a byte the workspace holds before init (default: whatever it held)."""
+    `fill`: a byte the workspace holds before init (default: whatever it held).
+    `splits`: workgroups per lane (0: the library's choice)."""
     q, k, v, kp, vp = inputs
     B, H, D = w.batch, w.heads, w.head_dim
     stream = torch.cuda.current_stream(dev)
@@ -57,6 +58,7 @@ def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, 
         ws = _workspace(nbytes, dev, fill)
         st = dsa.dsa_policy_state_init(policy, B, w.L_p, n_r, w.N_att, H, D, w.dtype, ws, nbytes, stream)
     dsa.dsa_set_waves(st, waves)
+    dsa.dsa_set_splits(st, splits)
     out = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
     trace = torch.empty((T, B, H, 2), dtype=torch.int32, device=dev)
     dsa.dsa_append_prompt(st, kp if w.L_p else None, vp if w.L_p else None)

@@ -56,6 +56,7 @@ def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
     lanes = B * H
     stride = (N_att - S + 7) // 8 * 8      # per-lane list padded to 16 bytes
     want = _align(lanes * (L_p + N_r) * row) + _align(lanes * stride * 2)
+    want += _align(lanes * 4 * (D + 8) * 4) + _align(lanes * 4)  # split records (up to 4 per lane), counters
     assert dsa.dsa_state_workspace_bytes(B, L_p, N_r, N_att, H, D, S, dt) == want
     assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * row)
 
@@ -178,3 +179,27 @@ def test_null_state_and_handle():
     assert lib.dsa_state_step(None) == E_INVAL
     assert lib.dsa_state_destroy(None) == OK
     assert lib.dsa_state_init(None, 1, 1, 4, 2, 1, 64, 0, 0, ctypes.c_void_p(FAKE_WS), 1 << 30, None) == E_INVAL
+
+
+def test_split_count_is_validated():
+    args = (2, 16, 32, 8, 3, 128, 0, 1)
+    st = dsa.dsa_state_init(*args, FAKE_WS, dsa.dsa_state_workspace_bytes(*args))
+    for n in (3, 8, -1):
+        with pytest.raises(DsaError) as e:
+            dsa.dsa_set_splits(st, n)
+        assert e.value.code == E_INVAL
+    for n in (0, 1, 2, 4):
+        dsa.dsa_set_splits(st, n)
+    dsa.dsa_state_destroy(st)
+    # the other state kinds do not split (MXFP8 states neither; their init
+    # clears the cache on the device, so that case runs in the GPU tests)
+    pargs = (dsa.DSA_POLICY_TOVA, 2, 16, 8, 8, 3, 128, 1)
+    st = dsa.dsa_policy_state_init(*pargs, FAKE_WS, dsa.dsa_policy_workspace_bytes(*pargs))
+    dst = dsa.dense_state_init(1, 0, 4, 2, 64, 1, FAKE_WS, 1 << 30)
+    for s in (st, dst):
+        for n in (0, 1):
+            dsa.dsa_set_splits(s, n)
+        with pytest.raises(DsaError) as e:
+            dsa.dsa_set_splits(s, 2)
+        assert e.value.code == E_INVAL
+        dsa.dsa_state_destroy(s)

@@ -33,11 +33,12 @@ def tiny(**kw):
     return synth.WORKLOADS["tiny_fp32"].with_(**kw)
 
 
-def _parity(w, T=None, lanes=None, waves=0, read_every=0, layer=0):
+def _parity(w, T=None, lanes=None, waves=0, read_every=0, layer=0, splits=0):
     T = w.L_dec if T is None else T
-    say("parity %s T=%d N_r=%d N_att=%d sink=%d waves=%d" % (w.name, T, w.N_r, w.N_att, w.sink, waves))
+    say("parity %s T=%d N_r=%d N_att=%d sink=%d waves=%d splits=%d" % (w.name, T, w.N_r, w.N_att, w.sink, waves,
+                                                                       splits))
     ins = device_inputs(w, layer, T, DEV)
-    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every)
+    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, splits=splits)
     lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
     stats = {}
     for (b, h) in lanes:

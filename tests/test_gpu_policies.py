@@ -45,13 +45,14 @@ def offsets_of(mask_row, t_next):
     return sorted(t_next - p for p in np.nonzero(mask_row)[0])
 
 
-def check_policy(policy, w, lanes=None, waves=0, read_every=0, layer=0, T=None, fill=None):
+def check_policy(policy, w, lanes=None, waves=0, read_every=0, layer=0, T=None, fill=None, splits=0):
     T = w.L_dec if T is None else T
     n_r = n_r_for(policy, w)
-    say("policy %s %s T=%d N_att=%d N_r=%d waves=%d fill=%s" % (NAMES[policy], w.name, T, w.N_att, n_r, waves, fill))
+    say("policy %s %s T=%d N_att=%d N_r=%d waves=%d fill=%s splits=%d" % (NAMES[policy], w.name, T, w.N_att, n_r,
+                                                                          waves, fill, splits))
     ins = device_inputs(w, layer, T, DEV)
     out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, policy=policy, N_r=n_r,
-                                   fill=fill)
+                                   fill=fill, splits=splits)
     lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
     stats = {"near_ties": 0, "choices": 0, "max_err": 0.0}
     for (b, h) in lanes:

@@ -1,0 +1,132 @@
+"""GPU parity of split launches: 2 or 4 workgroups per lane, each over one
+contiguous slice of the lane's attended rows, the last of them to finish
+merging the partial softmax states and argmin candidates in slice order
+(dsa_set_splits).  Every check is against the CPU oracle, in lockstep, as for
+one workgroup per lane; and the split and unsplit launches must make the same
+choices and evictions, bit for bit, with outputs equal up to fp32 rounding."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_image_generation_amd as dsa
+import synth
+from gpu_util import device_inputs, run_sparse
+from test_gpu_parity import _parity, _sample_lanes
+from test_gpu_policies import check_policy
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def tiny(**kw):
+    return synth.WORKLOADS["tiny_fp32"].with_(**kw)
+
+
+@pytest.mark.parametrize("splits,waves", [(2, 1), (2, 4), (4, 1), (4, 2), (4, 16)])
+def test_tiny_fp32_every_lane_and_step(splits, waves):
+    _parity(tiny(), waves=waves, splits=splits, read_every=1)
+
+
+def test_tiny_fp32_sink4():
+    _parity(tiny(sink=4), splits=4, read_every=1)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(L_p=0),                         # step 0 attends one row: three of four slices are empty
+    dict(N_att=1),
+    dict(N_att=2, N_r=3),
+    dict(N_att=5, N_r=6, sink=4),
+    dict(batch=7, heads=3, L_p=5),       # ragged lanes and slices
+])
+def test_edge_cases(kw):
+    _parity(tiny(**kw), splits=4, read_every=3)
+
+
+@pytest.mark.parametrize("dt,D", [(synth.BF16, 64), (synth.BF16, 128), (synth.F32, 128)])
+def test_dtypes_and_head_dims(dt, D):
+    _parity(tiny(dtype=dt, head_dim=D, batch=3, heads=5), splits=2, read_every=5)
+
+
+@pytest.mark.parametrize("policy", [dsa.DSA_POLICY_SLIDING_WINDOW, dsa.DSA_POLICY_STREAMING_LLM])
+def test_position_policies(policy):
+    check_policy(policy, tiny(N_att=24), splits=4, read_every=4)
+
+
+def test_same_choices_as_one_workgroup_per_lane():
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=2, heads=3)
+    ins = device_inputs(w, 0, w.L_dec, DEV)
+    o1, t1, _ = run_sparse(w, ins, w.L_dec, DEV, waves=2, splits=1)
+    worst = 0.0
+    for splits in (2, 4):
+        o2, t2, _ = run_sparse(w, ins, w.L_dec, DEV, waves=2, splits=splits)
+        np.testing.assert_array_equal(t2, t1)
+        worst = max(worst, float((o2 - o1).abs().max()))
+    say("  max |split - unsplit| = %.3g" % worst)
+    assert worst <= 1e-5
+
+
+def test_deterministic_and_counters_reset():
+    """The merge order is fixed (slice order, whichever workgroup finishes
+    last), so two runs agree bit for bit; switching the split count between
+    steps keeps working, since every split launch leaves its counters at 0."""
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=2)
+    ins = device_inputs(w, 0, w.L_dec, DEV)
+    o1, t1, _ = run_sparse(w, ins, w.L_dec, DEV, splits=4)
+    o2, t2, _ = run_sparse(w, ins, w.L_dec, DEV, splits=4)
+    assert torch.equal(o1, o2)
+    np.testing.assert_array_equal(t1, t2)
+
+    q, k, v, kp, vp = ins
+    B, H, D = w.batch, w.heads, w.head_dim
+    nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.current_stream(DEV)
+    st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes, stream)
+    dsa.dsa_append_prompt(st, kp, vp)
+    out = torch.empty((w.L_dec, B, H, D), dtype=torch.float32, device=DEV)
+    tr = torch.empty((w.L_dec, B, H, 2), dtype=torch.int32, device=DEV)
+    for t in range(w.L_dec):
+        dsa.dsa_set_splits(st, (4, 2, 1, 0)[t % 4])
+        dsa.dsa_append_decode_step(st, k[t], v[t], q[t], out[t], tr[t])
+    torch.cuda.synchronize(DEV)
+    dsa.dsa_state_destroy(st)
+    np.testing.assert_array_equal(tr.cpu().numpy(), t1)
+    assert float((out - o1).abs().max()) <= 1e-5
+
+
+def test_mxfp8_states_do_not_split():
+    w = tiny(dtype=synth.MXFP8, head_dim=128)
+    B, H, D = w.batch, w.heads, w.head_dim
+    nbytes = dsa.dsa_state_workspace_bytes(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    st = dsa.dsa_state_init(B, w.L_p, w.N_r, w.N_att, H, D, w.sink, w.dtype, ws, nbytes,
+                            torch.cuda.current_stream(DEV))
+    for n in (0, 1):
+        dsa.dsa_set_splits(st, n)
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_set_splits(st, 2)
+    torch.cuda.synchronize(DEV)
+    dsa.dsa_state_destroy(st)
+
+
+def test_largest_attended_list():
+    """8192 window offsets, four slices of sixteen-wavefront workgroups."""
+    w = tiny(batch=1, heads=2, L_p=4, N_r=8200, N_att=8192, L_dec=8201)
+    _, _, stats = _parity(w, waves=16, splits=4)
+    assert stats["selections"] == 2 * 8
+
+
+@pytest.mark.parametrize("name,splits", [("janus_pro_1b", 2), ("lumina_mgpt_7b_1024", 2),
+                                         ("hires_8100_sink4", 4)])
+def test_full_size_workload_sampled_lanes(name, splits):
+    """Full batch x heads x L_dec of one layer with split launches; the oracle
+    checks a seeded sample of lanes over every step."""
+    w = synth.WORKLOADS[name]
+    _parity(w, lanes=_sample_lanes(w, 2, 11), layer=w.layers - 1, splits=splits)
