@@ -730,6 +730,8 @@ int dsa_set_splits(dsa_state* st, int splits_per_lane) {
     if (splits_per_lane > 1 && (st->kind != KIND_SPARSE || st->dtype == DSA_MXFP8))
         return fail(DSA_E_INVAL, "only sparse states with bf16 or fp32 rows split (got a %s state, dtype %d)",
                     kind_name(st->kind), st->dtype);
+    if ((long long)st->lanes * splits_per_lane > 0x7fffffffll)
+        return fail(DSA_E_INVAL, "lanes * splits_per_lane exceeds the launch grid (%d lanes)", st->lanes);
     st->splits = splits_per_lane;
     return DSA_OK;
 }
