@@ -101,6 +101,19 @@ def test_deterministic_and_counters_reset():
     assert float((out - o1).abs().max()) <= 1e-5
 
 
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x7F])
+def test_workspace_garbage(fill):
+    """Whatever the workspace held before init (records, counters included)
+    never reaches a result: the counters are zeroed before the first split
+    launch and every record is written before it is read."""
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=2, heads=3)
+    ins = device_inputs(w, 0, w.L_dec, DEV)
+    o1, t1, _ = run_sparse(w, ins, w.L_dec, DEV, splits=1)
+    o2, t2, _ = run_sparse(w, ins, w.L_dec, DEV, splits=4, fill=fill)
+    np.testing.assert_array_equal(t2, t1)
+    assert float((o2 - o1).abs().max()) <= 1e-5
+
+
 def test_mxfp8_states_do_not_split():
     w = tiny(dtype=synth.MXFP8, head_dim=128)
     B, H, D = w.batch, w.heads, w.head_dim
