@@ -46,6 +46,8 @@ struct dsa_state {
     int batch, heads, D, L_p, N_r, N_att, S, dtype, L_max;
     int lanes, N_rw, N_attw, list_stride;
     long long lane_rows;
+    long long scale_rows;  // MXFP8: scale words per lane (the lane's cache rows)
+    size_t scale_off;      // MXFP8: byte offset of the scale-word region (right after the cache rows)
     char* ws;
     size_t ws_bytes;
     size_t list_off;
@@ -66,10 +68,15 @@ struct dsa_state {
 
 namespace {
 
-// Bytes of one cache row (K then V): plain elements, or MXFP8 codes plus the
-// 8-byte word of E8M0 block scales.
+// Bytes of one cache row (K then V): plain elements, or MXFP8 codes (the
+// row's 8-byte word of E8M0 block scales is kept in a region of its own).
 size_t row_bytes(int D, int dtype) {
-    return dtype == DSA_MXFP8 ? (size_t)2 * D + 8 : (size_t)2 * D * (dtype == DSA_BF16 ? 2 : 4);
+    return dtype == DSA_MXFP8 ? (size_t)2 * D : (size_t)2 * D * (dtype == DSA_BF16 ? 2 : 4);
+}
+
+// MXFP8 states: one 8-byte scale word per cache row, [lanes][rows per lane].
+size_t scale_bytes(long long lanes, long long rows, int dtype) {
+    return dtype == DSA_MXFP8 ? ((size_t)lanes * (size_t)rows * 8 + 255) / 256 * 256 : 0;
 }
 
 // Per-lane list entries, padded so every lane's list starts on 16 bytes.
@@ -183,6 +190,8 @@ int launch_prompt(dsa_state* st, const void* k_p, const void* v_p) {
         a.list = init_list ? reinterpret_cast<int16_t*>(st->ws + st->list_off) : nullptr;
         a.counter = nullptr;
         a.lane_rows = st->lane_rows;
+        a.scales = st->ws + st->scale_off;
+        a.scale_rows = st->scale_rows;
         a.B = st->batch;
         a.H = st->heads;
         a.L_p = st->L_p;
@@ -223,6 +232,8 @@ void fill_common(const dsa_state* st, const void* q_t, float* out, dsa::DecodeAr
     a.v_new = st->pend_v;
     a.out = out;
     a.lane_rows = st->lane_rows;
+    a.scales = st->ws + st->scale_off;
+    a.scale_rows = st->scale_rows;
     a.lanes = st->lanes;
     a.L_p = st->L_p;
     a.t = st->t;
@@ -268,6 +279,7 @@ int check_score(int policy, int batch, int L_p, int N_att, int heads, int head_d
 size_t score_workspace_bytes(int policy, int batch, int L_p, int N_att, int heads, int head_dim, int dtype) {
     const long long lanes = (long long)batch * heads;
     size_t b = kv_bytes(lanes, (long long)L_p + N_att, head_dim, dtype) +
+               scale_bytes(lanes, (long long)L_p + N_att, dtype) +
                align_up((size_t)lanes * (size_t)meta_stride_for(N_att) * sizeof(int32_t));
     if (policy == DSA_POLICY_H2O) b += align_up((size_t)lanes * (size_t)score_stride_for(N_att) * sizeof(double));
     return b;
@@ -339,7 +351,7 @@ size_t dsa_state_workspace_bytes(int batch, int L_p, int N_r, int N_att, int hea
                                  int dtype) {
     if (check_sparse(batch, L_p, N_r, N_att, heads, head_dim, sink, dtype)) return 0;
     const long long lanes = (long long)batch * heads;
-    return kv_bytes(lanes, (long long)L_p + N_r, head_dim, dtype) +
+    return kv_bytes(lanes, (long long)L_p + N_r, head_dim, dtype) + scale_bytes(lanes, (long long)L_p + N_r, dtype) +
            align_up((size_t)lanes * (size_t)list_stride_for(N_att - sink) * sizeof(int16_t)) +
            split_rec_bytes(lanes, head_dim) + counter_bytes(lanes);
 }
@@ -373,7 +385,9 @@ int dsa_state_init(dsa_state** out, int batch, int L_p, int N_r, int N_att, int 
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
     st->ring_off = (size_t)st->lanes * (size_t)L_p * row_bytes(head_dim, dtype);
-    st->list_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
+    st->scale_rows = (long long)L_p + N_r;
+    st->scale_off = kv_bytes(st->lanes, (long long)L_p + N_r, head_dim, dtype);
+    st->list_off = st->scale_off + scale_bytes(st->lanes, st->scale_rows, dtype);
     st->part_off = st->list_off + align_up((size_t)st->lanes * (size_t)st->list_stride * sizeof(int16_t));
     st->ctr_off = st->part_off + split_rec_bytes(st->lanes, head_dim);
     st->stream = static_cast<hipStream_t>(hip_stream);
@@ -429,7 +443,9 @@ int dsa_policy_state_init(dsa_state** out, int policy, int batch, int L_p, int N
     st->ws_bytes = workspace_bytes;
     st->meta_stride = meta_stride_for(N_att);
     st->score_stride = score_stride_for(N_att);
-    st->meta_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    st->scale_rows = st->lane_rows;
+    st->scale_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    st->meta_off = st->scale_off + scale_bytes(st->lanes, st->scale_rows, dtype);
     st->score_off = st->meta_off + align_up((size_t)st->lanes * (size_t)st->meta_stride * sizeof(int32_t));
     st->n_recent = policy == DSA_POLICY_H2O ? N_r : 0;
     st->stream = static_cast<hipStream_t>(hip_stream);
@@ -571,7 +587,8 @@ int dsa_read_state(const dsa_state* st, int32_t* h_t, int16_t* h_offsets, int32_
 
 size_t dense_state_workspace_bytes(int batch, int L_p, int L_max, int heads, int head_dim, int dtype) {
     if (check_common(batch, L_p, heads, head_dim, dtype) || L_max < 1) return 0;
-    return kv_bytes((long long)batch * heads, (long long)L_p + L_max, head_dim, dtype);
+    return kv_bytes((long long)batch * heads, (long long)L_p + L_max, head_dim, dtype) +
+           scale_bytes((long long)batch * heads, (long long)L_p + L_max, dtype);
 }
 
 int dense_state_init(dsa_state** out, int batch, int L_p, int L_max, int heads, int head_dim, int dtype,
@@ -598,7 +615,9 @@ int dense_state_init(dsa_state** out, int batch, int L_p, int L_max, int heads, 
     st->ws = static_cast<char*>(d_workspace);
     st->ws_bytes = workspace_bytes;
     st->stream = static_cast<hipStream_t>(hip_stream);
-    rc = clear_mx_rows(st, kv_bytes(st->lanes, st->lane_rows, head_dim, dtype));
+    st->scale_rows = st->lane_rows;
+    st->scale_off = kv_bytes(st->lanes, st->lane_rows, head_dim, dtype);
+    rc = clear_mx_rows(st, st->scale_off + scale_bytes(st->lanes, st->scale_rows, dtype));
     if (rc) {
         delete st;
         return rc;

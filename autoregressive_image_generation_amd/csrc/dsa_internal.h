@@ -32,6 +32,11 @@ struct DecodeArgs {
     float* out;            // [lanes][D]
     int32_t* trace;        // sparse, nullable: [lanes][2]
     long long lane_rows;   // rows per lane in the cache
+    // MXFP8 states: the 8-byte scale word of every cache row, lane-major:
+    // [lanes][scale_rows], row index r of the lane's rows (sparse: prompt rows
+    // 0 .. L_p-1, then L_p + ring index)
+    char* scales;
+    long long scale_rows;
     int lanes;
     int L_p;
     int S;                 // sink count (0 or 4)
@@ -75,6 +80,8 @@ struct PromptArgs {
     const void* v_p;
     void* kv;
     int16_t* list;         // nullable: when set, list[lane * list_stride] = 0 for every lane
+    char* scales;          // MXFP8: scale words [lanes][scale_rows] (as in DecodeArgs)
+    long long scale_rows;
     int32_t* counter;      // nullable: when set, counter[lane] = 0 for every lane
     long long lane_rows;
     int B, H, L_p, list_stride;

@@ -147,7 +147,7 @@ struct Mx8 {
     static constexpr int EPT = 16;
     template <int D>
     static constexpr size_t row_bytes() {
-        return (size_t)2 * D + 8;
+        return (size_t)2 * D;  // the codes; the scale word lives apart (DecodeArgs::scales)
     }
     struct Chunk {
         uint4 k, v;
@@ -323,6 +323,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         const bool listed = r >= win0;
         bool self;
         const char* row;
+        long long sidx;  // MXFP8: the row's index among the lane's scale words
         d = -1;
         if constexpr (MODE == MODE_SPARSE) {
             // Offsets are written only by this kernel and lie in [0, N_rw);
@@ -336,27 +337,31 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             const char* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * RB;
             const char* rrow = ring + ((size_t)ri * a.lanes + lane) * RB;
             row = r < a.L_p ? prow : rrow;
+            sidx = r < a.L_p ? min(r, max(a.L_p - 1, 0)) : a.L_p + ri;
             d = listed ? dl : -1;
         } else if constexpr (MODE == MODE_DENSE) {
             self = r >= a.L_p && r - a.L_p == a.t;
             row = lane_kv + (size_t)r * RB;
+            sidx = r;
         } else {
             const int j = max(r - win0, 0);
             const bool me = j == a.n_occ;
             const int slot = min(j + (j >= fslot ? 1 : 0), a.N_cache - 1);
             self = listed && me;
-            row = lane_kv + (size_t)(listed ? a.L_p + slot : r) * RB;
+            sidx = listed ? a.L_p + slot : r;
+            row = lane_kv + (size_t)sidx * RB;
             d = listed ? (me ? 0 : a.t - s_meta[4 + slot]) : -1;
         }
         if constexpr (MX) {
             d = self ? kSelfOutOfStream : d;  // the row address stays a valid cache row
             kr = row + sl * 16;
             vr = row + D + sl * 16;
-            sr = row + 2 * D;
+            sr = a.scales + ((size_t)lane * a.scale_rows + sidx) * 8;
         } else {
             kr = (self ? k_self : row) + sl * 16;
             vr = (self ? v_self : row + D * sizeof(T)) + sl * 16;
             sr = nullptr;
+            (void)sidx;
         }
     };
     auto load_row = [&](const char* kr, const char* vr, const char* sr) {
@@ -559,7 +564,10 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                 const int off = tid < CH / 2 ? 8 * tid : D + 8 * (tid - CH / 2);
                 *reinterpret_cast<uint2*>(dst_row + off) = qcode;
             }
-            if (tid == 0) *reinterpret_cast<uint2*>(dst_row + 2 * D) = make_uint2(qw0, qw1);
+            if (tid == 0) {
+                const long long sidx = a.L_p + (MODE == MODE_SPARSE ? a.self_row : SLOTS ? fslot : a.self_row);
+                *reinterpret_cast<uint2*>(a.scales + ((size_t)lane * a.scale_rows + sidx) * 8) = make_uint2(qw0, qw1);
+            }
         } else {
             if (tid < CH) *reinterpret_cast<uint4*>(dst_row + tid * 16) = ax;
         }
@@ -891,7 +899,7 @@ __global__ void prompt_kernel(PromptArgs a) {
             uint4* dst = reinterpret_cast<uint4*>(row + half * D + blk * 32);
             dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
             dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-            row[2 * D + half * 4 + blk] = (char)(X + 127);
+            a.scales[(lane * (size_t)a.scale_rows + j) * 8 + half * 4 + blk] = (char)(X + 127);
         }
     } else {
         constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per half-row

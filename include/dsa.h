@@ -69,7 +69,9 @@ typedef enum {
  * rounded to nearest even and saturated at +-448); every decode row is
  * attended in its quantised form, the current token's included.  The pages
  * call KV quantization stackable with the selection (Section 6) and fix no
- * format.  A row then takes 2 * head_dim + 8 bytes instead of 4 * head_dim.
+ * format.  A row then takes 2 * head_dim bytes of codes instead of 4 * head_dim,
+ * plus its 8-byte scale word, kept in a region of its own (one word per cache
+ * row, lane-major), so that the codes of a row fill whole 64-byte segments.
  * The *_init calls of DSA_MXFP8 states clear the workspace's cache rows on
  * the state's stream (hipMemsetAsync), so whatever the workspace held before
  * never reaches the attention; the other dtypes enqueue nothing at init.

@@ -48,17 +48,22 @@ def _align(x):
     (8, 96, 4050, 810, 32, 128, 4, 1),
     (1, 16, 32, 8, 4, 64, 0, 0),
     (3, 0, 5, 5, 1, 64, 0, 1),
-    (96, 64, 288, 29, 32, 128, 0, 2),   # MXFP8 rows: 2 d codes + 8 scale bytes
+    (96, 64, 288, 29, 32, 128, 0, 2),   # MXFP8 rows: 2 d codes, and 8 scale bytes apart
     (2, 16, 32, 8, 3, 64, 4, 2),
 ])
 def test_workspace_size(B, L_p, N_r, N_att, H, D, S, dt):
-    row = 2 * D + 8 if dt == 2 else 2 * D * (2 if dt == 1 else 4)
+    row = 2 * D if dt == 2 else 2 * D * (2 if dt == 1 else 4)
     lanes = B * H
+
+    def scales(rows):  # MXFP8: the scale words, one 8-byte word per row, in a region of their own
+        return _align(lanes * rows * 8) if dt == 2 else 0
+
     stride = (N_att - S + 7) // 8 * 8      # per-lane list padded to 16 bytes
-    want = _align(lanes * (L_p + N_r) * row) + _align(lanes * stride * 2)
+    want = _align(lanes * (L_p + N_r) * row) + scales(L_p + N_r) + _align(lanes * stride * 2)
     want += _align(lanes * 4 * (D + 8) * 4) + _align(lanes * 4)  # split records (up to 4 per lane), counters
     assert dsa.dsa_state_workspace_bytes(B, L_p, N_r, N_att, H, D, S, dt) == want
-    assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == _align(lanes * (L_p + 576) * row)
+    assert dsa.dense_state_workspace_bytes(B, L_p, 576, H, D, dt) == (_align(lanes * (L_p + 576) * row) +
+                                                                      scales(L_p + 576))
 
 
 @pytest.mark.parametrize("args", [

@@ -59,7 +59,7 @@ def _parity(w, waves=0, read_every=0, layer=0, lanes=None, fill=None):
 
 
 def _quantised_rows(x):
-    """(codes, scales) of rows [..., d] as the cache lays a row out: K or V codes, then 8 scale bytes."""
+    """(codes, scales) of rows [..., d]: a row's K or V codes, and the 4 scale bytes of that half."""
     return oracle.quantize_mxfp8(bf16(x))
 
 
@@ -80,7 +80,7 @@ def test_cache_bytes_equal_the_oracle_quantisation(D, S):
     torch.cuda.synchronize(DEV)
     dsa.dsa_state_destroy(st)
     raw = ws.cpu().numpy()
-    RB = 2 * D + 8
+    RB = 2 * D                              # a row's codes: K then V
     lanes = B * H
     nb = D // 32
     host = {n: x.cpu().numpy().view(np.uint16) for n, x in zip(("q", "k", "v", "kp", "vp"), ins)}
@@ -88,17 +88,21 @@ def test_cache_bytes_equal_the_oracle_quantisation(D, S):
     prompt = raw[: lanes * L * RB].reshape(lanes, L, RB)
     # ring region: [N_r][lanes] rows; decode position p (< N_r here) sits at ring index p
     ring = raw[lanes * L * RB: lanes * (L + w.N_r) * RB].reshape(w.N_r, lanes, RB)
+    # scale words after the 256-byte aligned cache rows: [lanes][L_p + N_r] words of 8 bytes
+    # (byte 4 half + b: block b of K (half 0) or V (half 1)); row L_p + i is ring index i
+    off = (lanes * (L + w.N_r) * RB + 255) // 256 * 256
+    words = raw[off: off + lanes * (L + w.N_r) * 8].reshape(lanes, L + w.N_r, 8)
     for b in range(B):
         for h in range(H):
             lane = b * H + h
             for half, name in ((0, "kp"), (1, "vp")):
                 c, s = _quantised_rows(host[name][b, :, h, :])
                 np.testing.assert_array_equal(prompt[lane, :, half * D:(half + 1) * D], c)
-                np.testing.assert_array_equal(prompt[lane, :, 2 * D + 4 * half: 2 * D + 4 * half + nb], s)
+                np.testing.assert_array_equal(words[lane, :L, 4 * half: 4 * half + nb], s)
             for half, name in ((0, "k"), (1, "v")):
                 c, s = _quantised_rows(host[name][:, b, h, :])
                 np.testing.assert_array_equal(ring[:T, lane, half * D:(half + 1) * D], c)
-                np.testing.assert_array_equal(ring[:T, lane, 2 * D + 4 * half: 2 * D + 4 * half + nb], s)
+                np.testing.assert_array_equal(words[lane, L:L + T, 4 * half: 4 * half + nb], s)
 
 
 def test_tiny_all_phases():
