@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC = {
     # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
     # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.77e6, "kernel_sha256_16": "10acee0bdd10da79"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.76e6, "kernel_sha256_16": "95d0d8a1116d6233"},
     # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.47e6, "kernel_sha256_16": "10acee0bdd10da79"},
+    ("janus_pro_7b", 2): {"bytes_per_launch": 75.46e6, "kernel_sha256_16": "95d0d8a1116d6233"},
     # MXFP8 cache, two micro-batches of 48: dispatches 24000-24599 of its own decode kernel
-    # (steps 400-409), algorithmic 39.39 MB; its 264-byte rows straddle 64-byte segments
-    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 45.94e6, "kernel_sha256_16": "10acee0bdd10da79"},
+    # (steps 400-409), algorithmic 39.39 MB; a window row's scale word comes with a 64-byte segment
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.85e6, "kernel_sha256_16": "95d0d8a1116d6233"},
 }
 
 
@@ -96,7 +96,8 @@ def log(msg):
 
 # ----------------------------------------------------------------------------- byte model
 def row_bytes(w):
-    """Bytes of one cached K|V row: 2 d elements, or MXFP8 codes plus the 8-byte scale word."""
+    """Bytes of one cached K|V row: 2 d elements, or MXFP8 codes plus the 8-byte scale word
+    (stored apart from the codes, read with them)."""
     import synth
 
     if w.dtype == synth.MXFP8:
