@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     constexpr int RSTR = KeyStage<T, D>::RSTR;      // LDS row stride in 8-byte units
     const int tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
     const int lane = blockIdx.x / tiles;
-    const int wave = threadIdx.x / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: scalar branches below
     const int i0 = (blockIdx.x % tiles) * 16 * kMapWaves + 16 * wave;  // this wavefront's first query
     const int l = threadIdx.x % 64;
     const int col = l % 16, quarter = l / 16;
@@ -167,6 +167,10 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     // reference, its registers would be demoted to scratch memory)
     KeyStage<T, D> pf;
     const float scale = (float)(1.4426950408889634 / sqrt((double)D));  // log2(e) / sqrt(D)
+    // The keys causal for all of this wavefront's queries (0 .. first_key) and
+    // for any of them (0 .. last_key); a wavefront wholly past T has none.
+    const int first_key = i0 + 15 < a.T ? min(a.L_p + i0, ncols - 1) : -1;
+    const int last_key = a.L_p + min(i0 + 15, a.T - 1);
 
     // pass 1: this lane's online (max, sum) per query over its columns, then
     // the 16 lanes of each query merged
@@ -183,23 +187,32 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         __syncthreads();
         // unconditional (past the last key it rereads it): no merge of old and new registers
         pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
-        for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
-            const int c = c0 + 16 * tt + col;
-            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // causal keys only; the running maximum moves only when a
-                // logit passes it by more than 8 (log2 units), so a key
-                // costs one exp2, and (m, s) stays exact for any m it holds
-                const int i = i0 + 4 * quarter + e;
-                const bool ok = c < ncols && c <= a.L_p + i;
-                const float x = t[e] * scale;
-                const bool need = ok && !(x <= m[e] + 8.0f);
-                if (__builtin_amdgcn_ballot_w64(need)) {
-                    s[e] *= need ? __builtin_amdgcn_exp2f(m[e] - x) : 1.0f;
-                    m[e] = need ? x : m[e];
+        for (int tp = 0; tp < kMapKeys / 16; tp += 2) {
+            // two tiles' MFMA chains, then their softmax work
+            f32x4 ts[2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2)
+                ts[q2] = map_tile<T, D>(s_k + (16 * (tp + q2) + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int cmin = c0 + 16 * (tp + q2);
+                if (cmin >= ncols || cmin > last_key) break;
+                const int c = cmin + col;
+                const f32x4 t = ts[q2];
+                const bool full = cmin + 15 <= first_key;  // every key causal for every query (uniform)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + 4 * quarter + e;
+                    const bool ok = full || (c < ncols && c <= a.L_p + i);
+                    const float x = t[e] * scale;
+                    const bool need = ok && !(x <= m[e] + 8.0f);
+                    if (__builtin_amdgcn_ballot_w64(need)) {
+                        s[e] *= need ? __builtin_amdgcn_exp2f(m[e] - x) : 1.0f;
+                        m[e] = need ? x : m[e];
+                    }
+                    s[e] += ok ? __builtin_amdgcn_exp2f(x - m[e]) : 0.0f;
                 }
-                s[e] += ok ? __builtin_amdgcn_exp2f(x - m[e]) : 0.0f;
             }
         }
     }
@@ -222,20 +235,43 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         __syncthreads();
         // unconditional (past the last key it rereads it): no merge of old and new registers
         pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, c0 + kMapKeys);
-        for (int tt = 0; tt < kMapKeys / 16 && c0 + 16 * tt < ncols; ++tt) {
-            const int c = c0 + 16 * tt + col;
-            const f32x4 t = map_tile<T, D>(s_k + (16 * tt + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
-            const int j = c - a.L_p;  // decode position of the key
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = i0 + 4 * quarter + e;
-                const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
-                const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
-                const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
-                mp[e] += j < 0 ? p : 0.0f;
-                ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
-                mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
-                if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
+        for (int tp = 0; tp < kMapKeys / 16; tp += 2) {
+            f32x4 ts[2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2)
+                ts[q2] = map_tile<T, D>(s_k + (16 * (tp + q2) + col) * (RSTR * 8 / (int)sizeof(T)) + M::PER * quarter, qa);
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int cmin = c0 + 16 * (tp + q2);
+                if (cmin >= ncols || cmin > last_key) break;
+                const int c = cmin + col;
+                const f32x4 t = ts[q2];
+                const int j = c - a.L_p;  // decode position of the key
+                const bool full = cmin + 15 <= first_key;
+                if (full && cmin + 15 < a.L_p) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mp[e] += __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e];
+                } else if (full && cmin >= a.L_p && cmin + 15 - a.L_p <= i0 - (i0 + 10) / 10) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e];
+                        mm[e] += p;
+                        P[(size_t)(i0 + 4 * quarter + e) * a.T + j] = p;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = i0 + 4 * quarter + e;
+                        const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
+                        const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
+                        const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
+                        mp[e] += j < 0 ? p : 0.0f;
+                        ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
+                        mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
+                        if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
+                    }
+                }
             }
         }
     }
