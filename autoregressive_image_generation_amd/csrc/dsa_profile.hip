@@ -248,6 +248,10 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
                 const int c = cmin + col;
                 const f32x4 t = ts[q2];
                 const int j = c - a.L_p;  // decode position of the key
+                // Uniform over the wavefront: every key of the tile causal for every
+                // query, and then all prompt keys, or all decode keys of every query's
+                // middle group (at most i - ceil((i + 1) / 10), which does not decrease
+                // with i): no masks, no mass-split selects.  Else the general path.
                 const bool full = cmin + 15 <= first_key;
                 if (full && cmin + 15 < a.L_p) {
 #pragma unroll
