@@ -10,9 +10,10 @@
  * ("Diagonal-Aware Sparse Attention"), its "Detailed explanation" (the worked
  * example with N_r = 7, N_att = 4) and Section 5.1 "Our methods" (the
  * Diagonal+Sink4 variant).  The method is a selection heuristic, not a faster
- * route to a closed form, so this file runs the algorithm step by step in the
- * pages' notation: absolute decode positions, an explicit skip_idx list that
- * is shifted by +1 each step, an explicit window, explicit eviction.  All
+ * route to a closed form, so this file runs the algorithm step by step with
+ * the pages' quantities: absolute decode positions, the skipped set as a list
+ * of positions that each move +1 per step, an explicit window and an explicit
+ * eviction.  All
  * arithmetic is fp64; the inputs are the exact fp32 / bf16 values the GPU
  * receives, widened without loss by the caller.
  *
@@ -24,9 +25,10 @@
  *   - eviction happens at step t before attention;
  *   - Attn is one softmax over the concatenation of prompt rows and the
  *     selected decode rows, scaled by 1 / sqrt(d), no other mask;
- *   - argmin_j softmax(...) is taken on the raw logits q . k (same order,
- *     no scaling that could merge values), ties go to the lowest position;
- *   - the candidates are the decode entries in idx at step t, the current
+ *   - the lowest-score entry is found on the raw logits q . k (softmax keeps
+ *     their order; no scaling that could merge values), ties go to the
+ *     lowest position;
+ *   - the candidates are the decode entries attended at step t, the current
  *     token included, prompt and sink entries excluded;
  *   - Diagonal+Sink4 (S = 4): decode positions 0..3 are sinks, attended from
  *     the step they exist on, never in the window, never evicted, never
@@ -64,21 +66,84 @@ static void attend(int d, const double* q, int n, const double** rows_k, const d
 }
 
 /*
+ * Lane state of the selection.  Decode positions are absolute (token t has
+ * position t); `skip` holds the positions of the skipped set in the order
+ * they were chosen, and moves along the attention diagonal by one position per
+ * step; `held` says which decode positions the cache still holds.
+ */
+struct lane {
+    int S;       /* sink count (0 or 4) */
+    int Nr_w;    /* window length over non-sink positions, N_r - S */
+    int room;    /* how many positions the skipped set may hold, N_r - N_att */
+    int nskip;
+    int32_t* skip;
+    uint8_t* held;
+};
+
+/*
+ * Which regime step t is in ([DAS] Section 4, Algorithm 1 and its "Detailed
+ * explanation"): every decode entry attended until N_att - 1 steps have run;
+ * then one entry joins the skipped set per step while the window grows; from
+ * t = N_r on the window slides and its oldest entry leaves the cache.
+ */
+enum regime { ATTEND_ALL = 1, GROW_SKIPS = 2, SLIDE_WINDOW = 3 };
+
+static enum regime regime_of(int t, int N_att, int N_r) {
+    if (t < N_att - 1) return ATTEND_ALL;
+    return t < N_r ? GROW_SKIPS : SLIDE_WINDOW;
+}
+
+/* The diagonal move: a position skipped for query t - 1 is skipped at its
+ * successor for query t (Algorithm 1, phases 2 and 3). */
+static void move_along_diagonal(struct lane* L) {
+    for (int j = 0; j < L->nskip; ++j) L->skip[j] += 1;
+}
+
+/* Phase 3: the non-sink entry that falls out of the window loses its K/V.
+ * Returns its position. */
+static int drop_oldest(struct lane* L, int t) {
+    int p = t - L->Nr_w;
+    L->held[p] = 0;
+    return p;
+}
+
+/*
+ * Decode positions step t attends, ascending: the sinks that exist by now,
+ * then every window position (non-sink, within the last Nr_w positions up to
+ * t itself) whose K/V is still held and that is not in the skipped set.
+ * `mark` is scratch of T bytes.  Returns the count; *nsink gets the sinks.
+ */
+static int attended_positions(const struct lane* L, int t, int T, uint8_t* mark, int32_t* pos, int* nsink) {
+    int n = 0;
+    for (int p = 0; p < L->S && p <= t; ++p) pos[n++] = p;
+    *nsink = n;
+    memset(mark, 0, (size_t)T);
+    for (int j = 0; j < L->nskip; ++j)
+        if (L->skip[j] >= 0 && L->skip[j] < T) mark[L->skip[j]] = 1;
+    int first = t - L->Nr_w;
+    if (first < L->S) first = L->S;
+    for (int p = first; p <= t; ++p)
+        if (L->held[p] && !mark[p]) pos[n++] = p;
+    return n;
+}
+
+/*
  * One lane, decode steps t = 0 .. T-1.
  *   Q, K, V     : [T][d] query / key / value of decode token t (K, V indexed by position)
  *   Kp, Vp      : [L_p][d] prompt keys / values
- *   follow      : optional [T]; at a selection step the position appended to
- *                 skip_idx is follow[t] instead of the oracle's own argmin
+ *   follow      : optional [T]; at a selection step the position added to the
+ *                 skipped set is follow[t] instead of the oracle's own choice
  *                 (lockstep with another implementation).  It must be a
  *                 candidate, else the call fails with -2.
  * Outputs (each [T], or [T][d] / [T][T]; the optional ones may be NULL):
  *   out         : attention output of step t
- *   choice      : the oracle's own argmin position at step t, -1 when no selection
+ *   choice      : the oracle's own lowest-score position at step t, -1 when no selection
  *   evicted     : position evicted at step t, -1 when none
  *   n_dec       : number of decode positions attended at step t (sinks included)
- *   gap         : optional; at selection steps with follow, (s[follow] - s[choice]) / max(|s|), else 0
+ *   gap         : optional; at selection steps with follow, (s[follow] - s[choice]) / max(|s[follow]|, |s[choice]|)
+ *                 on the raw logits, else 0
  *   att_mask    : optional; att_mask[t*T + p] = 1 iff decode position p is attended at step t
- *   skip_mask   : optional; skip_mask[t*T + p] = 1 iff p is in skip_idx when step t attends
+ *   skip_mask   : optional; skip_mask[t*T + p] = 1 iff p is in the skipped set when step t attends
  * Returns 0, -1 on invalid parameters, -2 on a follow entry that is not a candidate,
  * -3 on allocation failure.
  */
@@ -89,119 +154,98 @@ int oracle_dsa_lane(int L_p, int N_r, int N_att, int S, int d, int T, const doub
     if (L_p < 0 || d < 1 || T < 0 || N_att < 1 || N_r < N_att || (S != 0 && S != 4) || (S == 4 && N_att <= S))
         return -1;
     int rc = 0;
-    int32_t* skip_idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N_r + 1));
-    uint8_t* present = (uint8_t*)calloc((size_t)(T > 0 ? T : 1), 1);   /* decode KV held in the cache */
-    uint8_t* in_skip = (uint8_t*)calloc((size_t)(T > 0 ? T : 1), 1);
-    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T + 1));
+    struct lane L;
+    L.S = S;
+    L.Nr_w = N_r - S;
+    L.room = N_r - N_att;
+    L.nskip = 0;
+    L.skip = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N_r + 1));
+    L.held = (uint8_t*)calloc((size_t)(T > 0 ? T : 1), 1);
+    uint8_t* mark = (uint8_t*)calloc((size_t)(T > 0 ? T : 1), 1);
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T + 1));
     int nrows_max = L_p + S + T + 1;
     const double** rk = (const double**)malloc(sizeof(double*) * (size_t)nrows_max);
     const double** rv = (const double**)malloc(sizeof(double*) * (size_t)nrows_max);
     double* s = (double*)malloc(sizeof(double) * (size_t)nrows_max);
-    if (!skip_idx || !present || !in_skip || !idx || !rk || !rv || !s) {
+    if (!L.skip || !L.held || !mark || !pos || !rk || !rv || !s) {
         rc = -3;
         goto done;
     }
-    int nskip = 0;
-    int Nr_w = N_r - S; /* window length over non-sink positions */
 
     for (int t = 0; t < T; ++t) {
-        /* the new token's K, V enter the cache */
-        present[t] = 1;
+        enum regime ph = regime_of(t, N_att, N_r);
+        L.held[t] = 1; /* token t's K/V joins the cache */
         choice[t] = -1;
         evicted[t] = -1;
         if (gap) gap[t] = 0.0;
 
-        /* window <- [max(0, t - N_r), ..., t]  (non-sink positions) */
-        int lo = t - Nr_w;
-        if (lo < S) lo = S;
-        int select = 0;
+        if (ph != ATTEND_ALL) move_along_diagonal(&L);
+        if (ph == SLIDE_WINDOW) evicted[t] = drop_oldest(&L, t);
 
-        if (t < N_att - 1) {
-            /* Phase 1: full attention, idx <- window */
-        } else if (t < N_r) {
-            /* Phase 2: skip_idx <- [j + 1 for j in skip_idx]; idx <- window - skip_idx */
-            for (int j = 0; j < nskip; ++j) skip_idx[j] += 1;
-            if (nskip < N_r - N_att) select = 1;
-        } else {
-            /* Phase 3: K[t - N_r], V[t - N_r] <- empty; shift skip_idx by +1 */
-            int e = t - Nr_w;
-            present[e] = 0;
-            evicted[t] = e;
-            for (int j = 0; j < nskip; ++j) skip_idx[j] += 1;
-        }
+        int nsink = 0;
+        int npos = attended_positions(&L, t, T, mark, pos, &nsink);
+        n_dec[t] = npos;
 
-        /* idx <- window - skip_idx (only entries that still hold KV) */
-        memset(in_skip, 0, (size_t)T);
-        for (int j = 0; j < nskip; ++j)
-            if (skip_idx[j] >= 0 && skip_idx[j] < T) in_skip[skip_idx[j]] = 1;
-        int nidx = 0;
-        for (int p = lo; p <= t; ++p)
-            if (!in_skip[p] && present[p]) idx[nidx++] = p;
-
-        /* rows: prompt KV, sink KV that exists by now, then K[idx] */
+        /* the prompt rows, then the attended decode rows, in one softmax */
         int n = 0;
         for (int j = 0; j < L_p; ++j, ++n) {
             rk[n] = Kp + (size_t)j * d;
             rv[n] = Vp + (size_t)j * d;
         }
-        int nsink = 0;
-        for (int p = 0; p < S && p <= t; ++p, ++n, ++nsink) {
-            rk[n] = K + (size_t)p * d;
-            rv[n] = V + (size_t)p * d;
-        }
-        int first_idx_row = n;
-        for (int j = 0; j < nidx; ++j, ++n) {
-            rk[n] = K + (size_t)idx[j] * d;
-            rv[n] = V + (size_t)idx[j] * d;
+        for (int j = 0; j < npos; ++j, ++n) {
+            rk[n] = K + (size_t)pos[j] * d;
+            rv[n] = V + (size_t)pos[j] * d;
         }
         attend(d, Q + (size_t)t * d, n, rk, rv, s, out + (size_t)t * d);
-        n_dec[t] = nsink + nidx;
 
         if (att_mask) {
             uint8_t* row = att_mask + (size_t)t * T;
             memset(row, 0, (size_t)T);
-            for (int p = 0; p < nsink; ++p) row[p] = 1;
-            for (int j = 0; j < nidx; ++j) row[idx[j]] = 1;
+            for (int j = 0; j < npos; ++j) row[pos[j]] = 1;
         }
         if (skip_mask) {
             uint8_t* row = skip_mask + (size_t)t * T;
             memset(row, 0, (size_t)T);
-            for (int j = 0; j < nskip; ++j) row[skip_idx[j]] = 1;
+            for (int j = 0; j < L.nskip; ++j) row[L.skip[j]] = 1;
         }
 
-        if (select) {
-            /* w <- softmax(Q_t K[idx]^T); j* <- argmin_j w[j]: the lowest raw logit,
-             * first (lowest position) among equals since idx ascends */
+        /* Phase 2 while the skipped set has room: the attended window entry
+         * with the lowest score joins it (it is still attended at this step).
+         * Softmax preserves the order of the raw logits, so the lowest logit
+         * is compared; scanning positions upward, the first (oldest) of equal
+         * logits wins.  Sinks are no candidates. */
+        if (ph == GROW_SKIPS && L.nskip < L.room) {
+            const double* sw = s + L_p + nsink; /* logits of the window entries */
+            const int32_t* pw = pos + nsink;
+            int nw = npos - nsink;
             int best = 0;
-            for (int j = 1; j < nidx; ++j)
-                if (s[first_idx_row + j] < s[first_idx_row + best]) best = j;
-            int jstar = idx[best];
-            choice[t] = jstar;
-            int app = jstar;
+            for (int j = 1; j < nw; ++j)
+                if (sw[j] < sw[best]) best = j;
+            choice[t] = pw[best];
+            int joins = pw[best];
             if (follow) {
-                int f = follow[t], found = -1;
-                for (int j = 0; j < nidx; ++j)
-                    if (idx[j] == f) found = j;
+                int found = -1;
+                for (int j = 0; j < nw; ++j)
+                    if (pw[j] == follow[t]) found = j;
                 if (found < 0) {
                     rc = -2;
                     goto done;
                 }
                 if (gap) {
-                    double a = s[first_idx_row + found], b = s[first_idx_row + best];
+                    double a = sw[found], b = sw[best];
                     double mag = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
                     gap[t] = mag > 0.0 ? (a - b) / mag : 0.0;
                 }
-                app = f;
+                joins = follow[t];
             }
-            /* skip_idx.append(idx[j*]) */
-            skip_idx[nskip++] = app;
+            L.skip[L.nskip++] = joins;
         }
     }
 done:
-    free(skip_idx);
-    free(present);
-    free(in_skip);
-    free(idx);
+    free(L.skip);
+    free(L.held);
+    free(mark);
+    free(pos);
     free(rk);
     free(rv);
     free(s);

@@ -260,6 +260,38 @@ def test_follow_own_choices_reproduces_run_and_zero_gaps():
     np.testing.assert_array_equal(a["out"], b["out"])
 
 
+@pytest.mark.parametrize("S", [0, 4])
+def test_gap_of_forced_choices_matches_numpy(S):
+    """The lockstep gap (Section 4, Algorithm 1, phase 2 selection; the near-tie
+    reading) is (s[follow] - s[own choice]) / max(|s[follow]|, |s[own choice]|)
+    on the raw logits.  Forcing the highest-logit candidate at every selection
+    step (candidates from the offset closed form, not from the oracle) makes
+    every gap positive and large; numpy recomputes both logits.  A flipped
+    sign, a min in the denominator or a gap taken against the wrong entry fails."""
+    w = _tiny()
+    q, kp, vp, k, v = oracle.lane_inputs(w, 0, 0, 2)
+    T = w.L_dec
+    sel = set(selection_steps(w.N_r, w.N_att))
+    follow = np.full(T, -1, np.int32)
+    own = {}
+    for t in range(T):
+        if t in sel:
+            cands = [p for p in attended_sets(t + 1, w.N_r, w.N_att, S, list(follow[:t]) + [-1])[t] if p >= S]
+            logits = [float(np.dot(q[t], k[p])) for p in cands]
+            follow[t] = cands[int(np.argmax(logits))]
+            own[t] = min(zip(logits, cands))[1]
+    r = oracle.run_lane(w.L_p, w.N_r, w.N_att, S, q, kp, vp, k, v, follow=np.maximum(follow, 0))
+    for t in range(T):
+        if t not in sel:
+            assert r["gap"][t] == 0.0 and r["choice"][t] == -1
+            continue
+        assert r["choice"][t] == own[t], t
+        a, b = float(np.dot(q[t], k[follow[t]])), float(np.dot(q[t], k[own[t]]))
+        want = (a - b) / max(abs(a), abs(b))
+        assert want > 1e-3, t
+        assert r["gap"][t] == pytest.approx(want, rel=1e-9), t
+
+
 def test_parameter_validation():
     z = np.zeros((4, 4))
     zp = np.zeros((1, 4))
