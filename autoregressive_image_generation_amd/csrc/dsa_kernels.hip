@@ -26,14 +26,15 @@
 //     thread's chunk is 16 bytes of K and 16 of V.
 //   Mx8 (the low-bit KV cache; Section 6 of the pages calls KV quantization
 //     stackable with the selection): MXFP8 of the OCP Microscaling v1.0
-//     format.  K codes (D bytes, E4M3), V codes (D bytes), then an 8-byte
-//     scale word: byte b the E8M0 scale of K block b, byte 4 + b that of V
-//     block b, blocks of 32 elements.  A thread's chunk is 16 codes of K, 16
-//     of V and the scale word (16-byte loads, as for the other formats: the
-//     per-row cost of the loop, not the bytes, bounds a row this short).  q and the appended K/V arrive in bf16; the
-//     appended row is quantised in the launch that appends it, and every
-//     decode row the attention reads, the current token's included, is the
-//     quantised one.
+//     format.  A row is K codes (D bytes, E4M3) then V codes (D bytes), whole
+//     64-byte segments at D = 128; its 8-byte scale word (byte b the E8M0
+//     scale of K block b, byte 4 + b that of V block b, blocks of 32
+//     elements) lives in a region of its own, one word per cache row,
+//     lane-major (DecodeArgs::scales).  A thread's chunk is 16 codes of K, 16
+//     of V (16-byte loads) and the row's scale word.  q and the appended K/V
+//     arrive in bf16; the appended row is quantised in the launch that
+//     appends it, and every decode row the attention reads, the current
+//     token's included, is the quantised one.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -675,35 +676,33 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                     best_j = s_bj[w];
                 }
             }
-            // The record goes out with device-coherent stores (written through
-            // to the point where the XCDs meet), and the arrival counter is a
-            // device-scope atomic issued after those stores have completed; the
-            // last workgroup reads the records back the same coherent way.  No
-            // cache-wide write-back or invalidate is needed.
+            // Publication by release / acquire at device (agent) scope: the
+            // record's stores, an agent-scope release fence executed by the
+            // whole of wave 0 (the lanes that stored), then the arrival as an
+            // acq_rel read-modify-write of the lane's counter.  The workgroup
+            // whose arrival completes the count takes an agent-scope acquire
+            // fence before it reads the other records, so every record it reads
+            // happens-before its loads (the counter's RMWs form one release
+            // sequence).
             float* rec = a.partial + (size_t)blockIdx.x * split_rec_floats(D);
             if (wl < TPR) {
 #pragma unroll
-                for (int e = 0; e < EPT; ++e)
-                    __hip_atomic_store(rec + sl * EPT + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int e = 0; e < EPT; ++e) rec[sl * EPT + e] = acc[e];
             }
             if (wl == 0) {
-                __hip_atomic_store(rec + D, sm.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(rec + D + 1, sm.l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<double*>(rec + D + 2), best_s, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<int*>(rec) + D + 4, best_d, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<int*>(rec) + D + 5, best_j, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                rec[D] = sm.m;
+                rec[D + 1] = sm.l;
+                *reinterpret_cast<double*>(rec + D + 2) = best_s;
+                reinterpret_cast<int*>(rec)[D + 4] = best_d;
+                reinterpret_cast<int*>(rec)[D + 5] = best_j;
             }
-            __builtin_amdgcn_s_waitcnt(0);            // the record's stores have completed
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // and the compiler keeps them first
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             int arrived = 0;
             if (wl == 0)
-                arrived = __hip_atomic_fetch_add(a.counter + lane, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                arrived = __hip_atomic_fetch_add(a.counter + lane, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
             arrived = __shfl(arrived, 0);
             if (arrived != nsplit - 1) return;
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             if (wl == 0) __hip_atomic_store(a.counter + lane, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // the records merged in split order (the argmin order is total)
             sm = Softmax{kNegBig, 0.0f};
@@ -712,22 +711,16 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             best_s = __builtin_inf();
             best_d = best_j = -1;
             for (int s2 = 0; s2 < nsplit; ++s2) {
-                float* r2 = a.partial + ((size_t)lane * nsplit + s2) * split_rec_floats(D);
+                const float* r2 = a.partial + ((size_t)lane * nsplit + s2) * split_rec_floats(D);
                 if (wl < TPR) {
                     float acc2[EPT];
 #pragma unroll
-                    for (int e = 0; e < EPT; ++e)
-                        acc2[e] = __hip_atomic_load(r2 + sl * EPT + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float m2 = __hip_atomic_load(r2 + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float l2 = __hip_atomic_load(r2 + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    merge<EPT>(sm, acc, m2, l2, acc2);
+                    for (int e = 0; e < EPT; ++e) acc2[e] = r2[sl * EPT + e];
+                    merge<EPT>(sm, acc, r2[D], r2[D + 1], acc2);
                 }
-                const double bs2 =
-                    __hip_atomic_load(reinterpret_cast<double*>(r2 + D + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int bd2 =
-                    __hip_atomic_load(reinterpret_cast<int*>(r2) + D + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int bj2 =
-                    __hip_atomic_load(reinterpret_cast<int*>(r2) + D + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const double bs2 = *reinterpret_cast<const double*>(r2 + D + 2);
+                const int bd2 = reinterpret_cast<const int*>(r2)[D + 4];
+                const int bj2 = reinterpret_cast<const int*>(r2)[D + 5];
                 if (bd2 >= 0 && (best_d < 0 || better(bs2, bd2, best_s, best_d))) {
                     best_s = bs2;
                     best_d = bd2;
@@ -772,8 +765,10 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         if constexpr (MODE == MODE_SPARSE) {
             int16_t* lst = a.list + (size_t)lane * a.list_stride;
             if (a.select) {
-                // skip_idx.append(idx[j*]): offset best_d leaves the attended list
-                // for good; the offset entering the window at t+1 takes its place.
+                // The lowest-scoring entry joins the skipped set: its offset best_d
+                // leaves the attended list for good (a skip keeps its offset as it
+                // moves along the diagonal), and the offset entering the window at
+                // t+1 takes its list entry.
                 if (best_j >= 0) {
                     chosen = a.t - best_d;
                     lst[best_j] = (int16_t)a.add_off;

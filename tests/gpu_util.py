@@ -39,9 +39,20 @@ def _workspace(nbytes, dev, fill):
     return torch.full((nbytes,), fill, dtype=torch.uint8, device=dev)
 
 
-def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, fill=None, splits=0):
+def check_steps(w, T):
+    """Steps whose attended sets the parity tests read back: both ends of each
+    phase of Algorithm 1 (Section 4), the step after each boundary, one step
+    inside phase 2, and the last step."""
+    mid = (w.N_att - 1 + w.N_r - 2) // 2
+    c = {0, 1, w.N_att - 2, w.N_att - 1, w.N_att, mid, w.N_r - 2, w.N_r - 1, w.N_r, w.N_r + 1, T - 1}
+    return sorted(x for x in c if 0 <= x < T)
+
+
+def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, fill=None, splits=0, read_at=()):
     """T steps of one layer.  Returns out [T][B][H][D] (device), trace [T][B][H][2]
-    (host) and, with read_every > 0, {t: (offsets, counts)} read after step t.
+    (host) and {t: (offsets, counts)}, the lane lists dsa_read_state gives after
+    step t (t = -1: before the first step): after every read_every-th step and
+    the last one (read_every > 0), and before each step c in read_at.
     With `policy` the state comes from dsa_policy_state_init (N_r defaults to w.N_r).
     `fill`: a byte the workspace holds before init (default: whatever it held).
     `splits`: workgroups per lane (0: the library's choice)."""
@@ -67,7 +78,12 @@ def run_sparse(w, inputs, T, dev, waves=0, read_every=0, policy=None, N_r=None, 
     step_tr = trace[0].numel() * 4
     qb, kb, vb, ob, tb = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), trace.data_ptr()
     reads = {}
+    before = set(read_at)
     for t in range(T):
+        if t in before:
+            t_next, offs, cnt = dsa.dsa_read_state(st)
+            assert t_next == t
+            reads[t - 1] = (offs.copy(), cnt.copy())
         dsa.dsa_append_kv(st, kb + t * step_in, vb + t * step_in)
         dsa.dsa_decode_step(st, qb + t * step_in, ob + t * step_out, tb + t * step_tr)
         if read_every and (t % read_every == 0 or t == T - 1):
@@ -100,15 +116,48 @@ def lane_inputs_from(w, layer, b, h, T):
     return oracle.lane_inputs(w, layer, b, h, T)
 
 
-def check_lane(w, ins, out_lane, trace_lane, stats):
+def check_reads(w, ref, reads, lane, T, stats=None):
+    """The GPU's attended lists against the oracle's own sets, bit for bit.
+
+    reads[t] holds the lists dsa_read_state gave after step t: the window
+    entries step c = t + 1 attends, as offsets c - position.  With the sinks
+    that exist by step c they must equal the oracle's attended decode set of
+    step c (att_mask), and the live window (the last N_r - S non-sink
+    positions up to c) minus them must equal its skipped set (skip_mask)
+    (Section 4, Algorithm 1: the attended set is the window less the skipped
+    set, phase 3 less the evicted entry)."""
+    S, Nrw = w.sink, w.N_r - w.sink
+    for t, (offs, cnt) in reads.items():
+        c = t + 1
+        if c >= T:
+            continue
+        n = int(cnt[lane])
+        row = [int(x) for x in offs[lane]]
+        assert n == (min(c - S + 1, w.N_att - S) if c >= S else 0), (c, n)
+        assert all(x == -1 for x in row[n:]), (c, "padding")
+        got_off = row[:n]
+        assert got_off == sorted(set(got_off)) and all(0 <= x < Nrw for x in got_off), (c, got_off)
+        got = sorted(set(range(min(c + 1, S))) | {c - x for x in got_off})
+        want = np.nonzero(ref["att_mask"][c])[0].tolist()
+        assert got == want, "step %d lane %d: attended %s, oracle %s" % (c, lane, got, want)
+        live = set(range(max(S, c - Nrw + 1), c + 1))
+        skipped = sorted(live - set(got))
+        assert skipped == np.nonzero(ref["skip_mask"][c])[0].tolist(), "step %d lane %d: skipped set" % (c, lane)
+        if stats is not None:
+            stats["sets_checked"] = stats.get("sets_checked", 0) + 1
+
+
+def check_lane(w, ins, out_lane, trace_lane, stats, reads=None, lane=None):
     """Lockstep parity of one lane: the oracle follows the GPU's choices and
     reports its own; indices must agree except near-ties (relative logit gap
-    below 1e-6), which are counted; outputs within the dtype's tolerance."""
+    below 1e-6), which are counted; outputs within the dtype's tolerance.
+    With `reads` (run_sparse's read-backs) and the lane's index, every read
+    list is checked against the oracle's attended and skipped sets."""
     T = out_lane.shape[0]
     gpu_choice = trace_lane[:, 0].astype(np.int32)
     sel = gpu_choice >= 0
     follow = np.where(sel, gpu_choice, 0).astype(np.int32)
-    ref = oracle.run_lane(w.L_p, w.N_r, w.N_att, w.sink, *ins, follow=follow)
+    ref = oracle.run_lane(w.L_p, w.N_r, w.N_att, w.sink, *ins, follow=follow, masks=bool(reads))
     # selection happens at exactly the oracle's steps
     np.testing.assert_array_equal(sel, ref["choice"] >= 0)
     np.testing.assert_array_equal(trace_lane[:, 1], ref["evicted"])
@@ -122,6 +171,9 @@ def check_lane(w, ins, out_lane, trace_lane, stats):
     err = float(np.abs(out_lane.astype(np.float64) - ref["out"]).max()) if T else 0.0
     stats["max_err"] = max(stats.get("max_err", 0.0), err)
     assert err <= tol(w), "max |out - oracle| = %.3g > %.3g" % (err, tol(w))
+    if reads:
+        check_reads(w, ref, reads, lane, T, stats)
+        del ref["att_mask"], ref["skip_mask"]
     return ref
 
 

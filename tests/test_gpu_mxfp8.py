@@ -3,8 +3,9 @@
 * Bit-exact: every code and scale byte the library writes into the cache
   (prompt rows and appended rows) equals the oracle's quantisation of the same
   bf16 inputs; the workspace layout is the one the library documents (prompt
-  region [lanes][L_p] rows, ring region [N_r][lanes] rows, a row = K codes, V
-  codes, 8-byte scale word).
+  region [lanes][L_p] rows, ring region [N_r][lanes] rows, a row = K codes
+  then V codes; the rows' 8-byte scale words in a region of their own,
+  [lanes][L_p + N_r] words).
 * Lockstep: choices and evictions exactly as the oracle run on the quantised
   K / V (near-ties counted), outputs within 1e-3 (both sides attend the same
   dequantised values; the 2e-2 bf16 bound is the stated one, 1e-3 catches a
@@ -19,7 +20,7 @@ import torch
 import autoregressive_image_generation_amd as dsa
 import oracle
 import synth
-from gpu_util import check_lane, device_inputs, lane_inputs_from, run_dense, run_sparse
+from gpu_util import check_lane, check_steps, device_inputs, lane_inputs_from, run_dense, run_sparse
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -46,12 +47,14 @@ def _parity(w, waves=0, read_every=0, layer=0, lanes=None, fill=None):
         w.name, w.L_dec, w.N_r, w.N_att, w.sink, w.head_dim, waves, fill))
     T = w.L_dec
     ins = device_inputs(w, layer, T, DEV)
-    out, trace, _ = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, fill=fill)
+    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, fill=fill,
+                                   read_at=check_steps(w, T))
     lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
     stats = {}
     for (b, h) in lanes:
         li = lane_inputs_from(w, layer, b, h, T)
-        check_lane(w, li, out[:, b, h, :].cpu().numpy(), trace[:, b, h, :], stats)
+        check_lane(w, li, out[:, b, h, :].cpu().numpy(), trace[:, b, h, :], stats, reads=reads,
+                   lane=b * w.heads + h)
     say("  lanes=%d selections=%d near_ties=%d max_err=%.3g" % (len(lanes), stats["selections"],
                                                               stats["near_ties"], stats["max_err"]))
     assert stats["max_err"] <= MX_TOL

@@ -16,8 +16,8 @@ import autoregressive_image_generation_amd as dsa
 import oracle
 import synth
 from closed_form import attended_sets, falling_expected, rising_expected
-from gpu_util import (check_lane, device_inputs, final_offsets, lane_inputs_from, run_dense, run_sparse, tol,
-                      to_dev)
+from gpu_util import (check_lane, check_steps, device_inputs, final_offsets, lane_inputs_from, run_dense, run_sparse,
+                      tol, to_dev)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -33,26 +33,33 @@ def tiny(**kw):
     return synth.WORKLOADS["tiny_fp32"].with_(**kw)
 
 
-def _parity(w, T=None, lanes=None, waves=0, read_every=0, layer=0, splits=0):
+def _parity(w, T=None, lanes=None, waves=0, read_every=0, layer=0, splits=0, read_at=None):
+    """One layer of T steps through the C ABI; the sampled lanes (default: all)
+    in lockstep with the oracle.  The attended lists are read back before every
+    step in read_at (default: the phase boundaries, check_steps) and after every
+    read_every-th step, and compared with the oracle's attended and skipped
+    sets; with read_every also with the offset closed form."""
     T = w.L_dec if T is None else T
+    read_at = check_steps(w, T) if read_at is None else read_at
     say("parity %s T=%d N_r=%d N_att=%d sink=%d waves=%d splits=%d" % (w.name, T, w.N_r, w.N_att, w.sink, waves,
                                                                        splits))
     ins = device_inputs(w, layer, T, DEV)
-    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, splits=splits)
+    out, trace, reads = run_sparse(w, ins, T, DEV, waves=waves, read_every=read_every, splits=splits,
+                                   read_at=read_at)
     lanes = lanes or [(b, h) for b in range(w.batch) for h in range(w.heads)]
     stats = {}
     for (b, h) in lanes:
+        lane = b * w.heads + h
         li = lane_inputs_from(w, layer, b, h, T)
-        ref = check_lane(w, li, out[:, b, h, :].cpu().numpy(), trace[:, b, h, :], stats)
+        check_lane(w, li, out[:, b, h, :].cpu().numpy(), trace[:, b, h, :], stats, reads=reads, lane=lane)
         if read_every:
             choices = [int(c) for c in trace[:, b, h, 0]]
-            lane = b * w.heads + h
             for t, (offs, cnt) in reads.items():
                 want = final_offsets(w, t + 1, choices[: t + 1])
                 got = [int(x) for x in offs[lane][: cnt[lane]]]
                 assert got == want, (t, got, want)
-    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g" % (
-        len(lanes), stats["selections"], stats["near_ties"], stats["max_err"]))
+    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g attended/skipped sets checked=%d" % (
+        len(lanes), stats["selections"], stats["near_ties"], stats["max_err"], stats.get("sets_checked", 0)))
     return out, trace, stats
 
 
@@ -271,8 +278,10 @@ def test_full_size_workload_sampled_lanes(name):
 def test_full_size_every_lane_of_one_layer(name):
     """Every lane of one full layer (512 / 3072 / 512 / 256 lanes x all L_dec
     steps) in the benchmarked launch shape against the oracle: exact choice
-    and eviction traces, outputs within the bf16 bound (lockstep per lane, in
-    a thread pool).  "+mxfp8": the same with the MXFP8 cache."""
+    and eviction traces, every lane's attended list read back at the phase
+    boundaries (check_steps) equal to the oracle's attended and skipped sets,
+    outputs within the bf16 bound (lockstep per lane, in a thread pool).
+    "+mxfp8": the same with the MXFP8 cache."""
     from concurrent.futures import ThreadPoolExecutor
 
     base, _, kv = name.partition("+")
@@ -283,7 +292,7 @@ def test_full_size_every_lane_of_one_layer(name):
     T = w.L_dec
     say("every lane: %s layer %d (%d lanes)" % (name, layer, w.lanes))
     ins = device_inputs(w, layer, T, DEV)
-    out, trace, _ = run_sparse(w, ins, T, DEV)
+    out, trace, reads = run_sparse(w, ins, T, DEV, read_at=check_steps(w, T))
     host = {n: x.cpu().numpy().view(np.uint16) for n, x in zip(("q", "k", "v", "kp", "vp"), ins)}
     out = out.cpu().numpy()
 
@@ -295,7 +304,7 @@ def test_full_size_every_lane_of_one_layer(name):
             kp_, vp_, k_, v_ = (oracle.mxfp8_roundtrip(x) for x in (kp_, vp_, k_, v_))
         li = (q_, kp_, vp_, k_, v_)
         st = {}
-        check_lane(w, li, out[:, b, h, :], trace[:, b, h, :], st)
+        check_lane(w, li, out[:, b, h, :], trace[:, b, h, :], st, reads=reads, lane=lane)
         return st
 
     with ThreadPoolExecutor(16) as ex:
@@ -303,7 +312,10 @@ def test_full_size_every_lane_of_one_layer(name):
     sel = sum(s["selections"] for s in stats)
     ties = sum(s["near_ties"] for s in stats)
     err = max(s["max_err"] for s in stats)
-    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g" % (w.lanes, sel, ties, err))
+    sets = sum(s.get("sets_checked", 0) for s in stats)
+    say("  lanes=%d selections=%d near_ties=%d max_err=%.3g attended/skipped sets checked=%d" % (
+        w.lanes, sel, ties, err, sets))
+    assert sets == w.lanes * len([c for c in check_steps(w, T) if c < T])
 
 
 def test_dense_full_size_janus7b_batch32_sampled():
