@@ -4,18 +4,24 @@
 One step = one whole image decode: every decode token t = 0 .. L_dec-1 through
 every layer in model order (append K/V, then the fused sparse decode launch),
 for the whole batch, on synthetic grid-rotary inputs already resident in HBM.
-The default workload is the Janus-Pro-7B shape (batch 96, 30 layers, 32 heads x
-128, L_p 64, L_dec 576 on a 24x24 grid, N_r 288, N_att 29 = 95 % sparsity).
+The headline workload is the Janus-Pro-7B shape (batch 96, 30 layers, 32 heads
+x 128, L_p 64, L_dec 576 on a 24x24 grid, N_r 288, N_att 29 = 95 % sparsity).
 
-Printed: one JSON line with head-steps/s (batch x layers x heads x L_dec per
-second) and HBM GB/s of the decode split into two micro-batch streams; the
-roofline of the sparse kernel (the same decode on one stream, whole batch per
-launch, from HIP events on the launch stream) and of the two-stream aggregate;
-the dense kernel at batch 32 beside the sparse one at the same batch; the
-sparse-KV baselines at the same budget (SlidingWindow, StreamingLLM, TOVA,
-H2O); the MXFP8 cache; the attention-map characterization of one layer; the
-device's HBM read ceiling from a plain read probe; and the CPU oracle on a
-bounded sample of the same workload.
+Printed: one JSON line.  For the headline workload: head-steps/s (batch x
+layers x heads x L_dec per second) and HBM GB/s of the decode split into two
+micro-batch streams (`value`); the roofline of the sparse kernel (the same
+decode on one stream, whole batch per launch, from HIP events on the launch
+stream) and of the two-stream aggregate; the per-step launch time as the window
+fills and slides; the dense kernel at the same batch and at batch 32, each
+beside the sparse kernel at that batch; the last decode step alone, sparse at
+90 % and 95 % against dense (attention only, batch 32); the sparse-KV
+baselines at the same budget (SlidingWindow, StreamingLLM, TOVA, H2O); the
+MXFP8 cache; the sparsity sweep; the attention-map characterization of one
+layer; the device's HBM read ceiling from a plain read probe; and the CPU
+oracle on a bounded sample of the same workload.  Then one leg per other
+workload (Janus-Pro-1B, Lumina-mGPT 1024x1024, 8100 tokens + sink4), each with
+its two-stream rate, one-stream roofline, per-step series, same-batch dense
+comparison and CPU oracle sample.
 """
 from __future__ import annotations
 
@@ -48,6 +54,8 @@ TRAFFIC = {
     ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.85e6, "kernel_sha256_16": "95d0d8a1116d6233"},
 }
 
+LEG_WORKLOADS = "janus_pro_1b,lumina_mgpt_7b_1024,hires_8100_sink4"
+
 
 def kernel_sha16():
     import hashlib
@@ -67,18 +75,24 @@ def traffic_for(name, streams=1):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=3, help="timed full decodes")
-    p.add_argument("--warmup", type=int, default=1, help="untimed full decodes first")
-    p.add_argument("--workload", default="janus_pro_7b")
-    p.add_argument("--dense-batch", type=int, default=32, help="batch of the dense comparison (0: skip)")
-    p.add_argument("--waves", type=int, default=0, help="wavefronts per lane (0: library's choice)")
+    p.add_argument("--steps", type=int, default=3, help="timed full decodes of the headline workload")
+    p.add_argument("--warmup", type=int, default=1, help="untimed full decodes of the headline workload first")
+    p.add_argument("--workload", default="janus_pro_7b", help="the headline workload")
+    p.add_argument("--legs", default=LEG_WORKLOADS,
+                   help="comma-separated further workloads, one leg each ('none': headline only)")
+    p.add_argument("--leg-steps", type=int, default=3, help="timed decodes per leg and per comparison run")
+    p.add_argument("--dense-batch", type=int, default=32,
+                   help="batch of the extra dense comparison and of the last-step comparison (0: skip both)")
+    p.add_argument("--no-dense-full", action="store_true", help="skip the dense kernel at each workload's batch")
+    p.add_argument("--waves", type=int, default=0, help="wavefronts per lane (0: library's / measured choice)")
     p.add_argument("--streams", type=int, default=0,
                    help="micro-batches, each on its own stream (0: 2 when the batch is even, else 1)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work (0: skip)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-seconds of oracle work per workload (0: skip)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
-    p.add_argument("--sweep", action="store_true", help="also time the sparsity sweep {0,.5,.8,.9,.95}")
+    p.add_argument("--no-sweep", action="store_true", help="skip the sparsity sweep {0,.5,.8,.9,.95}")
     p.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 KV-cache leg")
     p.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling probe")
+    p.add_argument("--no-series", action="store_true", help="skip the per-step series decode")
     p.add_argument("--profile-dist", type=int, default=48,
                    help="attention-map characterization of layer 0 up to this query distance (0: skip)")
     p.add_argument("--no-policies", action="store_true",
@@ -225,6 +239,8 @@ class SparseModel:
     independent, so one's launch can overlap another's.
     """
 
+    dense = False
+
     def __init__(self, w, inputs, layers, dev, waves, batch=None, streams=1, policy=None, splits=0):
         import torch
 
@@ -237,12 +253,7 @@ class SparseModel:
         self.S = streams
         self.Bc = self.B // streams
         self.policy = policy
-        if policy is None:
-            self.nbytes = dsa.dsa_state_workspace_bytes(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink,
-                                                        w.dtype)
-        else:
-            self.nbytes = dsa.dsa_policy_workspace_bytes(policy, self.Bc, w.L_p, policy_n_r(w, policy), w.N_att,
-                                                         w.heads, w.head_dim, w.dtype)
+        self.nbytes = self._workspace_bytes()
         self.ws = [[torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
                    for _ in range(streams)]
         self.out = torch.empty((self.B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
@@ -250,6 +261,13 @@ class SparseModel:
         self.waves = waves
         self.splits = splits
         self.states = []  # [micro-batch][layer]
+
+    def _workspace_bytes(self):
+        w, dsa = self.w, self.dsa
+        if self.policy is None:
+            return dsa.dsa_state_workspace_bytes(self.Bc, w.L_p, w.N_r, w.N_att, w.heads, w.head_dim, w.sink, w.dtype)
+        return dsa.dsa_policy_workspace_bytes(self.policy, self.Bc, w.L_p, policy_n_r(w, self.policy), w.N_att,
+                                              w.heads, w.head_dim, w.dtype)
 
     def _init_state(self, ws, stream):
         w = self.w
@@ -280,26 +298,34 @@ class SparseModel:
             for layer, ws in enumerate(self.ws[c]):
                 st = self._init_state(ws, self.streams[c])
                 dsa.dsa_set_waves(st, self.waves)
-                dsa.dsa_set_splits(st, getattr(self, "splits", 0))
+                if not self.dense:
+                    dsa.dsa_set_splits(st, self.splits)
                 self._append_prompt(st, self.inputs.layers[layer], c)
                 row.append(st)
             self.states.append(row)
         torch.cuda.synchronize(self.dev)
 
-    def _decode_fn(self):
-        return self.dsa.library().dsa_decode_step
+    def free(self):
+        for row in self.states:
+            for st in row:
+                self.dsa.dsa_state_destroy(st)
+        self.states = []
+        self.ws = None
+        self.out = None
 
-    def decode(self):
-        """All L_dec steps through all layers, in model order per micro-batch: one
-        append-and-decode call per (step, layer, micro-batch)."""
+    def run(self, t0=0, t1=None, step_events=None):
+        """Steps t0 .. t1-1 through all layers, in model order per micro-batch:
+        one append-and-decode call per (step, layer, micro-batch).  With
+        step_events (one stream only), event t - t0 is recorded on the launch
+        stream before step t's launches and the last one after step t1 - 1."""
         dsa, w = self.dsa, self.w
+        t1 = w.L_dec if t1 is None else t1
         q0 = self.inputs.layers[0]["q"]
         es = q0.element_size()
         step_bytes = q0[0].numel() * es
         chunk = self.Bc * w.heads * w.head_dim
         lib = dsa.library()
-        dense = isinstance(self, DenseModel)
-        call = lib.dense_append_decode_step if dense else lib.dsa_append_decode_step
+        call = lib.dense_append_decode_step if self.dense else lib.dsa_append_decode_step
         # per (layer, micro-batch), in launch order: state and its input / output addresses
         plan = []
         for layer, x in enumerate(self.inputs.layers):
@@ -307,9 +333,13 @@ class SparseModel:
                 off = c * chunk * es  # micro-batch c: contiguous in [B][H][D]
                 plan.append((self.states[c][layer], x["k"].data_ptr() + off, x["v"].data_ptr() + off,
                              x["q"].data_ptr() + off, self.out.data_ptr() + c * chunk * 4))
-        for t in range(w.L_dec):
+        if step_events is not None and self.S != 1:
+            raise ValueError("per-step events need one stream")
+        for t in range(t0, t1):
             o = t * step_bytes
-            if dense:
+            if step_events is not None:
+                step_events[t - t0].record(self.streams[0])
+            if self.dense:
                 for st, kp, vp, qp, op in plan:
                     rc = call(st, kp + o, vp + o, qp + o, op)
                     if rc:
@@ -319,29 +349,21 @@ class SparseModel:
                     rc = call(st, kp + o, vp + o, qp + o, op, None)
                     if rc:
                         raise dsa.DsaError(rc, dsa.dsa_last_error())
+        if step_events is not None:
+            step_events[t1 - t0].record(self.streams[0])
 
 
 class DenseModel(SparseModel):
     """One dense state per layer (optionally per micro-batch and stream)."""
 
+    dense = True
+
     def __init__(self, w, inputs, layers, dev, waves, batch, streams=1):
-        import torch
+        super().__init__(w, inputs, layers, dev, waves, batch=batch, streams=streams)
 
-        import autoregressive_image_generation_amd as dsa
-
-        self.dsa, self.w, self.inputs, self.dev = dsa, w, inputs, dev
-        self.B = batch
-        if self.B % streams:
-            raise ValueError("batch %d does not split into %d micro-batches" % (self.B, streams))
-        self.S = streams
-        self.Bc = self.B // streams
-        self.nbytes = dsa.dense_state_workspace_bytes(self.Bc, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype)
-        self.ws = [[torch.empty(self.nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
-                   for _ in range(streams)]
-        self.out = torch.empty((batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
-        self.streams = [torch.cuda.current_stream(dev)] if streams == 1 else micro_batch_streams(dev, streams)
-        self.waves = waves
-        self.states = []
+    def _workspace_bytes(self):
+        w = self.w
+        return self.dsa.dense_state_workspace_bytes(self.Bc, w.L_p, w.L_dec, w.heads, w.head_dim, w.dtype)
 
     def _init_state(self, ws, stream):
         w = self.w
@@ -355,16 +377,24 @@ class DenseModel(SparseModel):
                                      x["vp"].data_ptr() + off if w.L_p else None)
 
 
+WARM_STEPS = 16  # a partial decode that loads the kernels and touches the workspaces
+
+
 def time_decodes(model, steps, warmup, dev):
-    """Warm-up decodes, then `steps` timed decodes, each bracketed by a device
-    synchronisation; returns (seconds per decode by host clock, by HIP events).
-    The events sit on the launch stream(s): with several micro-batch streams,
-    every stream waits for the start event and the stop event waits for all."""
+    """Warm-up decodes (warmup = 0: a partial decode of WARM_STEPS steps, so the
+    timed decodes never pay first-launch costs), then `steps` timed decodes,
+    each bracketed by a device synchronisation; returns (seconds per decode by
+    host clock, by HIP events).  The events sit on the launch stream(s): with
+    several micro-batch streams, every stream waits for the start event and the
+    stop event waits for all."""
     import torch
 
+    if warmup == 0:
+        model.reset()
+        model.run(0, min(WARM_STEPS, model.w.L_dec))
     for _ in range(warmup):
         model.reset()
-        model.decode()
+        model.run()
     torch.cuda.synchronize(dev)
     wall = ev = 0.0
     per_stream = [0.0] * len(model.streams)
@@ -379,7 +409,7 @@ def time_decodes(model, steps, warmup, dev):
         for s in model.streams:
             if s != main:
                 s.wait_event(start)
-        model.decode()
+        model.run()
         for s, e in zip(model.streams, ends):
             e.record(s)
             if s != main:
@@ -394,40 +424,53 @@ def time_decodes(model, steps, warmup, dev):
     return wall / steps, ev / steps
 
 
-def kernel_durations(model, layers, dev):
-    """One decode with an event pair around every sparse launch, on the stream the
-    library launches on (torch's current stream).  Returns per-step lists of
-    launch durations in seconds."""
+def step_seconds(model, dev):
+    """One decode on one stream (after a partial warm-up) with an event on the
+    launch stream before every step and after the last: per step t, the time of
+    its `layers` back-to-back launches.  One event per step, none around single
+    launches, so the series carries no per-launch event overhead."""
     import torch
 
     if model.S != 1:
         return None
-    model.reset()
     w = model.w
-    n = w.L_dec * layers
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-    dsa, lib = model.dsa, model.dsa.library()
-    q0 = model.inputs.layers[0]["q"]
-    step_bytes = q0[0].numel() * q0.element_size()
-    ptrs = [(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr()) for x in model.inputs.layers]
-    out = model.out.data_ptr()
-    i = 0
-    for t in range(w.L_dec):
-        off = t * step_bytes
-        for st, (qp, kp, vp) in zip(model.states[0], ptrs):
-            rc = lib.dsa_append_kv(st, kp + off, vp + off)
-            evs[2 * i].record()
-            rc |= lib.dsa_decode_step(st, qp + off, out, None)
-            evs[2 * i + 1].record()
-            if rc:
-                raise dsa.DsaError(rc, dsa.dsa_last_error())
-            i += 1
+    model.reset()
+    model.run(0, min(WARM_STEPS, w.L_dec))
+    model.reset()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(w.L_dec + 1)]
+    model.run(step_events=evs)
     torch.cuda.synchronize(dev)
-    per_step = []
-    for t in range(w.L_dec):
-        per_step.append([evs[2 * (t * layers + l)].elapsed_time(evs[2 * (t * layers + l) + 1]) * 1e-3
-                         for l in range(layers)])
-    return per_step
+    return [evs[t].elapsed_time(evs[t + 1]) * 1e-3 for t in range(w.L_dec)]
+
+
+def series_summary(w, per_step, layers):
+    """Mean launch duration (us) per phase and at ~48 steps spread over the decode
+    (plus the phase boundaries), from step_seconds."""
+    phase_us = {}
+    for name, lo, hi in (("phase1", 0, min(w.N_att - 1, w.L_dec)),
+                         ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
+                         ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
+        if hi > lo:
+            phase_us[name] = sum(per_step[lo:hi]) / ((hi - lo) * layers) * 1e6
+    marks = set(range(0, w.L_dec, max(1, w.L_dec // 48))) | {w.L_dec - 1}
+    marks |= {t for t in (w.N_att - 2, w.N_att - 1, w.N_r - 1, w.N_r) if 0 <= t < w.L_dec}
+    series = [[t, round(per_step[t] / layers * 1e6, 3)] for t in sorted(marks)]
+    return phase_us, series
+
+
+def library_waves(w, lanes, dtype=None):
+    """The library's wavefront choice for a launch of `lanes` lanes (its
+    choose_waves rule), used to size the launch-floor probe like the decode."""
+    import synth
+
+    dt = w.dtype if dtype is None else dtype
+    ept = 4 if dt == synth.F32 else 16 if dt == synth.MXFP8 else 8
+    gpw = 64 // (w.head_dim // ept)
+    rows = w.L_p + w.N_att
+    wv = 1
+    while wv < 8 and lanes * 2 * wv < 3072 and rows >= 4 * gpw * 2 * wv:
+        wv *= 2
+    return wv
 
 
 def hbm_read_ceiling(dev, nbytes=4 << 30, reps=10):
@@ -556,45 +599,6 @@ def characterize(w, inputs, dev, max_dist, reps=3):
                     "similarity: banded MFMA Gram products; per-lane means)"}
 
 
-def cpu_baseline(w, target_cpu_seconds):
-    """The oracle as it stands on a bounded, seeded sample of lanes (all L_dec
-    steps each), one lane per host thread; returns the JSON object.  Inputs are
-    generated outside the timed parts, in chunks so host memory stays small."""
-    from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
-
-    import oracle
-
-    threads = max(1, min(16, os.cpu_count() or 1))
-    rng = np.random.default_rng(0)
-    T = w.L_dec
-
-    def run(ins):
-        oracle.run_lane(w.L_p, w.N_r, w.N_att, w.sink, *ins)
-
-    probe_in = oracle.lane_inputs(w, 0, 0, 0, T)
-    t0 = time.perf_counter()
-    run(probe_in)
-    probe = time.perf_counter() - t0
-    n = max(threads, int(math.ceil(target_cpu_seconds / max(probe, 1e-4))))
-    n = min(n, 20000)
-    lanes = [(int(rng.integers(w.layers)), int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(n)]
-    chunk = threads * 32
-    wall = 0.0
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        for i in range(0, n, chunk):
-            inputs = [oracle.lane_inputs(w, *x, T) for x in lanes[i:i + chunk]]
-            t0 = time.perf_counter()
-            list(ex.map(run, inputs))
-            wall += time.perf_counter() - t0
-    rate = n * T / wall
-    return {"value": rate, "unit": "head-steps/s", "cores": threads, "kind": "oracle",
-            "sample": "%d seeded random (layer, batch, head) lanes x all %d decode steps of %s (fp64 C oracle, "
-                      "one lane per thread, %.1f s wall, ~%.0f CPU-s; one lane alone %.4f s)"
-                      % (n, T, w.name, wall, wall * threads, probe)}
-
-
 def summarize_trace(path):
     """Per kernel and launch shape: dispatches and mean / min / max duration,
     plus the busy time (union of dispatch intervals) of each launch shape."""
@@ -626,6 +630,301 @@ def summarize_trace(path):
         print(json.dumps(r))
 
 
+def cpu_baseline(w, target_cpu_seconds):
+    """The oracle as it stands on a bounded, seeded sample of lanes (all L_dec
+    steps each), one lane per host thread; returns the JSON object.  Inputs are
+    generated outside the timed parts, in chunks so host memory stays small.
+    Threads: the host's CPUs this process may use, at most 16 (the CPU share of
+    one GPU on the boxes it runs on)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    threads = max(1, min(16, usable))
+    rng = np.random.default_rng(0)
+    T = w.L_dec
+
+    def run(ins):
+        oracle.run_lane(w.L_p, w.N_r, w.N_att, w.sink, *ins)
+
+    probe_in = oracle.lane_inputs(w, 0, 0, 0, T)
+    t0 = time.perf_counter()
+    run(probe_in)
+    probe = time.perf_counter() - t0
+    n = max(threads, int(math.ceil(target_cpu_seconds / max(probe, 1e-4))))
+    n = min(n, 20000)
+    lanes = [(int(rng.integers(w.layers)), int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(n)]
+    chunk = threads * 32
+    wall = 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for i in range(0, n, chunk):
+            inputs = [oracle.lane_inputs(w, *x, T) for x in lanes[i:i + chunk]]
+            t0 = time.perf_counter()
+            list(ex.map(run, inputs))
+            wall += time.perf_counter() - t0
+    rate = n * T / wall
+    return {"value": rate, "unit": "head-steps/s", "cores": threads, "kind": "oracle",
+            "single_core_value": T / probe, "host_cpus": os.cpu_count(), "usable_cpus": usable,
+            "sample": "%d seeded random (layer, batch, head) lanes x all %d decode steps of %s (fp64 C oracle, "
+                      "one lane per thread on %d threads, %.1f s wall, ~%.0f CPU-s; one lane alone %.4f s)"
+                      % (n, T, w.name, threads, wall, wall * threads, probe)}
+
+
+def free_cuda():
+    import gc
+
+    import torch
+
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def measure_workload(w, dev, args, headline):
+    """One workload: the sparse decode on S micro-batch streams (the rate) and on
+    one stream (the kernel's roofline and its per-step series), and the dense
+    kernel at the same batch.  Returns (result dict, inputs)."""
+    import synth
+
+    layers = args.layers or w.layers
+    log("== %s: %d layers, batch %d, generating inputs" % (w.name, layers, w.batch))
+    inputs = Inputs(w, layers, dev)
+    log("inputs ready in %.1f s" % inputs.gen_seconds)
+    head_steps = w.batch * layers * w.heads * w.L_dec
+    S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
+    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    steps, warmup = (args.steps, args.warmup) if headline else (args.leg_steps, 0)
+    total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+    n_launch = w.L_dec * layers  # launches per stream
+    lanes = w.batch * w.heads
+
+    # The whole job: the decode split into S micro-batches on S streams.
+    sparse = SparseModel(w, inputs, layers, dev, waves, streams=S)
+    sec, sec_ev = time_decodes(sparse, steps, warmup, dev)
+    log("sparse (%d micro-batch streams): %.1f ms per decode (events %.1f ms)" % (S, sec * 1e3, sec_ev * 1e3))
+    per_stream_launch_s = sum(sparse.stream_seconds) / S / n_launch
+
+    # The kernel alone: the same decode on one stream.  Its launches run back
+    # to back, so the timed region's HIP events (recorded on the stream the
+    # library launches on) / the launches is the kernel's average launch
+    # duration, gaps included, which is what rocprofv3's kernel trace reports
+    # per dispatch.  With S streams, S launches overlap; the kernel trace
+    # cannot follow that (the profiler serialises much of the overlap), so the
+    # aggregate over streams is reported apart.
+    if S > 1:
+        sparse.free()
+        del sparse
+        free_cuda()
+        single = SparseModel(w, inputs, layers, dev, args.waves, streams=1)
+        s1, s1_ev = time_decodes(single, steps, warmup, dev)
+        log("sparse, one stream: %.1f ms per decode" % (s1 * 1e3))
+    else:
+        single, s1, s1_ev = sparse, sec, sec_ev
+    launch_s = s1_ev / n_launch
+    bytes_per_launch = total_bytes / n_launch
+    achieved = bytes_per_launch / launch_s / 1e9
+    log("sparse kernel alone: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
+    wv = args.waves or library_waves(w, lanes)
+    floor_us = launch_floor(dev, lanes, 64 * wv)
+    log("launch floor (near-empty kernel, %d x %d threads, graph replay): %.2f us" % (lanes, 64 * wv, floor_us))
+    phase_us, series = {}, None
+    if not args.no_series:
+        per_step = step_seconds(single, dev)
+        phase_us, series = series_summary(w, per_step, layers)
+    single.free()
+    del single
+    free_cuda()
+
+    res = {
+        "value": head_steps / sec,
+        "unit": "head-steps/s",
+        "ms_per_step": sec * 1e3,
+        "steps": steps,
+        "warmup": warmup if warmup else "partial decode of %d steps" % WARM_STEPS,
+        "dtype": "bf16" if w.dtype == synth.BF16 else "fp32",
+        "config": {"workload": w.name, "batch": w.batch, "layers": layers, "heads": w.heads,
+                   "head_dim": w.head_dim, "L_p": w.L_p, "L_dec": w.L_dec, "N_r": w.N_r, "N_att": w.N_att,
+                   "sink": w.sink, "sparsity": round(1 - w.N_att / w.L_dec, 4),
+                   "step": "one full image decode: L_dec tokens x layers, all lanes",
+                   "micro_batches": S,
+                   "waves_per_lane": waves or "library choice",
+                   "accumulation": "fp64 logits, fp32 softmax and PV"},
+        "hbm_gbs": total_bytes / sec / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(w.name),
+                     "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
+                     "avg_launch_us": launch_s * 1e6,
+                     "bytes_per_launch": bytes_per_launch,
+                     "launch_floor_us": floor_us,
+                     "achieved_above_floor": bytes_per_launch / (launch_s - floor_us * 1e-6) / 1e9,
+                     "us_per_launch_by_phase": phase_us,
+                     "us_per_launch_by_step": series},
+        "events_ms_per_step": sec_ev * 1e3,
+    }
+    if S > 1:
+        agg = total_bytes / sec_ev / 1e9
+        res["roofline_micro_batched"] = {
+            "achieved": agg, "frac": agg / HBM_PEAK_GBS, "unit": "GB/s", "streams": S,
+            "traffic": traffic_for(w.name, S),
+            "avg_launch_us_per_stream": per_stream_launch_s * 1e6,
+            "bytes_per_launch": total_bytes / n_launch / S,
+            "note": "S launches of one micro-batch each in flight at once; all algorithmic bytes / event time"}
+        res["single_stream"] = {"value": head_steps / s1, "ms_per_step": s1 * 1e3}
+
+    if not args.no_dense_full:
+        # the dense kernel at the same batch and in the same micro-batches; the
+        # long decodes (L_dec > 576) are timed once, after a partial warm-up
+        dsteps = args.leg_steps if w.L_dec <= 576 else 1
+        dense = DenseModel(w, inputs, layers, dev, args.waves, w.batch, streams=S)
+        dsec, _ = time_decodes(dense, dsteps, 0, dev)
+        dense.free()
+        del dense
+        free_cuda()
+        dbytes = sum(dense_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+        res["dense_same_batch"] = {
+            "batch": w.batch, "micro_batches": S, "value": head_steps / dsec, "unit": "head-steps/s",
+            "ms_per_step": dsec * 1e3, "steps": dsteps, "hbm_gbs": dbytes / dsec / 1e9,
+            "sparse_speedup": dsec / sec, "byte_ratio": dbytes / total_bytes,
+            "budget_ratio": (w.L_p + w.N_r) / (w.L_p + w.N_att)}
+        log("dense b%d: %.1f ms per decode -> sparse %.2fx (byte ratio %.2f)" % (
+            w.batch, dsec * 1e3, dsec / sec, dbytes / total_bytes))
+    return res, inputs
+
+
+def headline_extras(w, inputs, res, dev, args):
+    """What only the headline workload measures: the dense comparison at the
+    extra batch, the last decode step alone, the policies, the MXFP8 cache, the
+    characterization, the sweep and the read ceiling."""
+    import synth
+
+    layers = args.layers or w.layers
+    S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
+    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    head_steps = w.batch * layers * w.heads * w.L_dec
+    sec = res["ms_per_step"] * 1e-3
+    total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+    ls = args.leg_steps
+
+    if args.dense_batch and args.dense_batch < w.batch:
+        db = args.dense_batch
+        dS = S if db % S == 0 else 1
+        wb = w.with_(batch=db)
+        dense = DenseModel(wb, inputs, layers, dev, args.waves, db, streams=dS)
+        dsec, _ = time_decodes(dense, ls, 0, dev)
+        dense.free()
+        del dense
+        sparse_b = SparseModel(wb, inputs, layers, dev, args.waves, batch=db, streams=dS)
+        ssec, _ = time_decodes(sparse_b, ls, 0, dev)
+        sparse_b.free()
+        del sparse_b
+        free_cuda()
+        dsteps = db * layers * w.heads * w.L_dec
+        dbytes = sum(dense_bytes_per_head_step(w, t) for t in range(w.L_dec)) * db * w.heads * layers
+        sbytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * db * w.heads * layers
+        res["dense_batch_%d" % db] = {
+            "batch": db, "micro_batches": dS, "value": dsteps / dsec, "unit": "head-steps/s",
+            "hbm_gbs": dbytes / dsec / 1e9, "ms_per_step": dsec * 1e3,
+            "sparse_value": dsteps / ssec, "sparse_ms_per_step": ssec * 1e3, "sparse_hbm_gbs": sbytes / ssec / 1e9,
+            "sparse_speedup": dsec / ssec, "byte_ratio": dbytes / sbytes,
+            "budget_ratio": (w.L_p + w.N_r) / (w.L_p + w.N_att)}
+        log("dense b%d: %.1f ms per decode; sparse b%d %.1f ms -> %.2fx" % (db, dsec * 1e3, db, ssec * 1e3,
+                                                                           dsec / ssec))
+
+        # The last decode step alone (attention only), one stream, batch db:
+        # dense against sparse at 90 % and 95 % sparsity (N_att from the ratio),
+        # the mean launch over the layers at t = L_dec - 1.
+        last = {"batch": db, "t": w.L_dec - 1, "streams": 1}
+        dense = DenseModel(wb, inputs, layers, dev, args.waves, db, streams=1)
+        d_last = step_seconds(dense, dev)[-1] / layers
+        dense.free()
+        del dense
+        last["dense_us"] = d_last * 1e6
+        for sp in (0.9, 0.95):
+            n_att = synth.n_att_for(w.L_dec, sp)
+            ws_ = wb.with_(N_att=n_att)
+            m = SparseModel(ws_, inputs, layers, dev, args.waves, batch=db, streams=1)
+            s_last = step_seconds(m, dev)[-1] / layers
+            m.free()
+            del m
+            rows_d = w.L_p + w.L_dec
+            rows_s = w.L_p + n_att
+            last["sparse_%g" % sp] = {"N_att": n_att, "us": s_last * 1e6, "speedup": d_last / s_last,
+                                      "row_ratio": rows_d / rows_s}
+            log("last step b%d: dense %.2f us, sparse %.2f (N_att %d) -> %.2fx" % (db, d_last * 1e6, s_last * 1e6,
+                                                                                  n_att, d_last / s_last))
+        free_cuda()
+        res["last_step_attention_b%d" % db] = last
+
+    if not args.no_policies:
+        pol = []
+        for policy in range(6):
+            if policy in (1, 3) and w.N_att <= 4:
+                continue
+            m = SparseModel(w, inputs, layers, dev, waves, streams=S, policy=policy)
+            s_p, _ = time_decodes(m, ls, 0, dev)
+            b = sum(policy_bytes_per_head_step(w, policy, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+            pol.append({"policy": POLICY_NAMES[policy], "N_r": policy_n_r(w, policy), "N_att": w.N_att,
+                        "value": head_steps / s_p, "ms_per_step": s_p * 1e3, "hbm_gbs": b / s_p / 1e9,
+                        "workspace_gb": m.nbytes * S * layers / 1e9})
+            log("policy %s: %.1f ms per decode, %.0f GB/s" % (POLICY_NAMES[policy], s_p * 1e3, b / s_p / 1e9))
+            m.free()
+            del m
+        free_cuda()
+        res["policies"] = pol
+
+    if not args.no_mxfp8 and w.dtype == synth.BF16:
+        wm = w.with_(dtype=synth.MXFP8)
+        m = SparseModel(wm, inputs, layers, dev, waves, streams=S)
+        s_m, _ = time_decodes(m, ls, 0, dev)
+        b = sum(sparse_bytes_per_head_step(wm, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+        res["mxfp8_kv"] = {"value": head_steps / s_m, "unit": "head-steps/s", "ms_per_step": s_m * 1e3,
+                           "hbm_gbs": b / s_m / 1e9, "speedup_vs_bf16_kv": sec / s_m,
+                           "traffic_per_launch": traffic_for(w.name + "_mxfp8", S),
+                           "algorithmic_bytes_per_launch": b / (w.L_dec * layers * S),
+                           "byte_ratio": total_bytes / b, "workspace_gb": m.nbytes * S * layers / 1e9,
+                           "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
+        log("mxfp8 kv: %.1f ms per decode, %.0f GB/s, %.2fx the bf16 cache" % (s_m * 1e3, b / s_m / 1e9, sec / s_m))
+        m.free()
+        del m
+        free_cuda()
+
+    if args.profile_dist > 0:
+        res["characterization"] = characterize(w, inputs, dev, args.profile_dist)
+
+    if not args.no_sweep:
+        sweep = []
+        for sp in (0.0, 0.5, 0.8, 0.9, 0.95):
+            n_att = synth.n_att_for(w.L_dec, sp)
+            n_r = w.N_r if n_att <= w.N_r else w.L_dec
+            ws_ = w.with_(N_att=n_att, N_r=n_r)
+            m = SparseModel(ws_, inputs, layers, dev, args.waves, streams=S)
+            s, _ = time_decodes(m, ls, 0, dev)
+            b = sum(sparse_bytes_per_head_step(ws_, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
+            sweep.append({"sparsity": sp, "N_r": n_r, "N_att": n_att, "value": head_steps / s,
+                          "ms_per_step": s * 1e3, "hbm_gbs": b / s / 1e9})
+            log("sweep %.2f: %.1f ms" % (sp, s * 1e3))
+            m.free()
+            del m
+        free_cuda()
+        res["sweep"] = sweep
+
+    if not args.no_ceiling:
+        c = hbm_read_ceiling(dev)
+        res["hbm_read_ceiling"] = {
+            "kernel": "dsa_hbm_read_probe (16-byte non-temporal loads, grid-stride, 4 GiB, best launch shape)",
+            "GBs": c["GBs"], "frac_of_peak": c["GBs"] / HBM_PEAK_GBS,
+            "shape": {k: c[k] for k in ("blocks", "threads", "unroll")},
+            "sparse_one_stream_frac_of_ceiling": res["roofline"]["achieved"] / c["GBs"],
+            "sparse_micro_batched_frac_of_ceiling":
+                res["roofline_micro_batched"]["achieved"] / c["GBs"] if "roofline_micro_batched" in res else None}
+        log("hbm read ceiling: %.0f GB/s (%s)" % (c["GBs"], res["hbm_read_ceiling"]["shape"]))
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -636,7 +935,6 @@ def main():
               "GPUs with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import autoregressive_image_generation_amd as dsa
@@ -659,201 +957,55 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "reads": n, "writes": n, "launches": 5}), flush=True)
         return
 
+    t_start = time.perf_counter()
     w = synth.WORKLOADS[args.workload]
-    layers = args.layers or w.layers
-    log("bench: %s, %d layers, batch %d, generating inputs" % (w.name, layers, w.batch))
-    inputs = Inputs(w, layers, dev)
-    log("inputs ready in %.1f s" % inputs.gen_seconds)
-
-    head_steps = w.batch * layers * w.heads * w.L_dec
-    S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
-    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
-    total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
-    n_launch = w.L_dec * layers  # launches per stream
-
-    # The whole job: the decode split into S micro-batches on S streams.
-    sparse = SparseModel(w, inputs, layers, dev, waves, streams=S)
-    sec, sec_ev = time_decodes(sparse, args.steps, args.warmup, dev)
-    log("sparse (%d micro-batch streams): %.1f ms per decode (events %.1f ms)" % (S, sec * 1e3, sec_ev * 1e3))
-    per_stream_launch_s = sum(sparse.stream_seconds) / S / n_launch
-
-    # The kernel alone: the same decode on one stream.  Its launches run back
-    # to back, so the timed region's HIP events (recorded on the stream the
-    # library launches on) / the launches is the kernel's average launch
-    # duration, gaps included, which is what rocprofv3's kernel trace reports
-    # per dispatch.  With S streams, S launches overlap; the kernel trace
-    # cannot follow that (the profiler serialises much of the overlap), so the
-    # aggregate over streams is reported apart.
-    if S > 1:
-        del sparse
-        single = SparseModel(w, inputs, layers, dev, args.waves, streams=1)
-        s1, s1_ev = time_decodes(single, args.steps, args.warmup, dev)
-        log("sparse, one stream: %.1f ms per decode" % (s1 * 1e3))
+    res, inputs = measure_workload(w, dev, args, headline=True)
+    headline_extras(w, inputs, res, dev, args)
+    del inputs
+    free_cuda()
+    if args.cpu_seconds > 0:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:
-        single, s1, s1_ev = sparse, sec, sec_ev
-    launch_s = s1_ev / n_launch
-    bytes_per_launch = total_bytes / n_launch
-    achieved = bytes_per_launch / launch_s / 1e9
-    log("sparse kernel alone: %.2f us per launch over %d launches, %.0f GB/s" % (launch_s * 1e6, n_launch, achieved))
-    # the per-launch floor of a kernel with the same grid: the library's
-    # wavefront rule for one stream (whole batch per launch) fixes the block
-    lanes = w.batch * w.heads
-    wv = args.waves
-    if not wv:
-        ept = 4 if w.dtype == synth.F32 else 8
-        gpw = 64 // (w.head_dim // ept)
-        rows = w.L_p + w.N_att
-        wv = 1
-        while wv < 8 and lanes * 2 * wv < 3072 and rows >= 4 * gpw * 2 * wv:
-            wv *= 2
-    floor_us = launch_floor(dev, lanes, 64 * wv)
-    log("launch floor (near-empty kernel, %d x %d threads, graph replay): %.2f us" % (lanes, 64 * wv, floor_us))
-    # per-phase latency from one decode with an event pair around every launch
-    # (each pair adds ~2 us of event overhead; for the step profile only)
-    durs = kernel_durations(single, layers, dev)
-    del single
-    phase_us = {}
-    for name, lo, hi in [] if durs is None else (("phase1", 0, min(w.N_att - 1, w.L_dec)),
-                                                 ("phase2", max(w.N_att - 1, 0), min(w.N_r, w.L_dec)),
-                                                 ("phase3", min(w.N_r, w.L_dec), w.L_dec)):
-        if hi > lo:
-            phase_us[name] = sum(sum(durs[t]) for t in range(lo, hi)) / ((hi - lo) * layers) * 1e6
-    # per-step latency as the window fills and slides: the mean launch over the
-    # layers at ~48 evenly spaced steps (and the phase boundaries)
-    step_series = None
-    if durs is not None:
-        marks = set(range(0, w.L_dec, max(1, w.L_dec // 48))) | {w.L_dec - 1}
-        marks |= {t for t in (w.N_att - 2, w.N_att - 1, w.N_r - 1, w.N_r) if 0 <= t < w.L_dec}
-        step_series = [[t, round(sum(durs[t]) / layers * 1e6, 3)] for t in sorted(marks)]
+        res["cpu_baseline"] = None
 
+    legs = {}
+    for name in [] if args.legs in ("", "none") else args.legs.split(","):
+        if name == w.name:
+            continue
+        wl = synth.WORKLOADS[name]
+        leg, leg_inputs = measure_workload(wl, dev, args, headline=False)
+        del leg_inputs
+        free_cuda()
+        if args.cpu_seconds > 0:
+            leg["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        legs[name] = leg
+        log("leg %s: %.3g head-steps/s, one stream %.3f of peak, two streams %.3f" % (
+            name, leg["value"], leg["roofline"]["frac"],
+            leg.get("roofline_micro_batched", leg["roofline"])["frac"]))
+
+    layers = args.layers or w.layers
     result = {
         "metric": "sparse decode-attn steps/s (batch x layers x heads) + HBM GB/s, Janus-Pro-7B shape",
-        "value": head_steps / sec,
-        "unit": "head-steps/s",
+        "value": res.pop("value"),
+        "unit": res.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": sec * 1e3,
+        "ms_per_step": res.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == synth.BF16 else "fp32",
+        "dtype": res.pop("dtype"),
         "data": "synthetic grid-rotary Q/K/V + N(0,0.1) noise, seed 0, resident in HBM",
-        "config": {"workload": w.name, "batch": w.batch, "layers": layers, "heads": w.heads,
-                   "head_dim": w.head_dim, "L_p": w.L_p, "L_dec": w.L_dec, "N_r": w.N_r, "N_att": w.N_att,
-                   "sink": w.sink, "sparsity": round(1 - w.N_att / w.L_dec, 4),
-                   "step": "one full image decode: L_dec tokens x layers, all lanes",
-                   "micro_batches": S,
-                   "waves_per_lane": waves or "library choice",
-                   "accumulation": "fp64 logits, fp32 softmax and PV"},
-        "hbm_gbs": total_bytes / sec / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(w.name),
-                     "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
-                     "avg_launch_us": launch_s * 1e6,
-                     "bytes_per_launch": bytes_per_launch,
-                     "launch_floor_us": floor_us,
-                     "achieved_above_floor": bytes_per_launch / (launch_s - floor_us * 1e-6) / 1e9,
-                     "event_pair_us_by_phase": phase_us,
-                     "event_pair_us_by_step": step_series},
-        "events_ms_per_step": sec_ev * 1e3,
+        "config": res.pop("config"),
     }
-    if S > 1:
-        agg = total_bytes / sec_ev / 1e9
-        result["roofline_micro_batched"] = {
-            "achieved": agg, "frac": agg / HBM_PEAK_GBS, "unit": "GB/s", "streams": S,
-            "traffic": traffic_for(w.name, S),
-            "avg_launch_us_per_stream": per_stream_launch_s * 1e6,
-            "bytes_per_launch": total_bytes / n_launch / S,
-            "note": "S launches of one micro-batch each in flight at once; all algorithmic bytes / event time"}
-        result["single_stream"] = {"value": head_steps / s1, "ms_per_step": s1 * 1e3}
-
-    if args.dense_batch:
-        db = min(args.dense_batch, w.batch)
-        dS = S if db % S == 0 else 1
-        dense = DenseModel(w, inputs, layers, dev, args.waves, db, streams=dS)
-        dsec, _ = time_decodes(dense, args.steps, args.warmup, dev)
-        dsteps = db * layers * w.heads * w.L_dec
-        dbytes = sum(dense_bytes_per_head_step(w, t) for t in range(w.L_dec)) * db * w.heads * layers
-        sparse_b = SparseModel(w, inputs, layers, dev, args.waves, batch=db, streams=dS)
-        ssec, _ = time_decodes(sparse_b, args.steps, args.warmup, dev)
-        result["dense"] = {"batch": db, "micro_batches": dS, "value": dsteps / dsec, "unit": "head-steps/s",
-                           "hbm_gbs": dbytes / dsec / 1e9,
-                           "ms_per_step": dsec * 1e3, "sparse_same_batch_value": dsteps / ssec,
-                           "sparse_speedup": dsec / ssec,
-                           "byte_ratio": dbytes / (sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec))
-                                                   * db * w.heads * layers),
-                           # the headline sparse decode (full batch) against the dense kernel at
-                           # this batch, per head-step, next to (L_p + N_r) / (L_p + N_att)
-                           "sparse_headline_vs_dense": (head_steps / sec) / (dsteps / dsec),
-                           "budget_ratio": (w.L_p + w.N_r) / (w.L_p + w.N_att)}
-        log("dense b%d: %.1f ms per decode; sparse b%d %.1f ms -> %.2fx" % (db, dsec * 1e3, db, ssec * 1e3,
-                                                                           dsec / ssec))
-        del dense, sparse_b
-
-    if not args.no_policies:
-        pol = []
-        for policy in range(6):
-            if policy == 1 and w.N_att <= 4 or policy == 3 and w.N_att <= 4:
-                continue
-            m = SparseModel(w, inputs, layers, dev, waves, streams=S, policy=policy)
-            s_p, _ = time_decodes(m, args.steps, args.warmup, dev)
-            b = sum(policy_bytes_per_head_step(w, policy, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
-            pol.append({"policy": POLICY_NAMES[policy], "N_r": policy_n_r(w, policy), "N_att": w.N_att,
-                        "value": head_steps / s_p, "ms_per_step": s_p * 1e3, "hbm_gbs": b / s_p / 1e9,
-                        "workspace_gb": m.nbytes * S * layers / 1e9})
-            log("policy %s: %.1f ms per decode, %.0f GB/s" % (POLICY_NAMES[policy], s_p * 1e3, b / s_p / 1e9))
-            del m
-        result["policies"] = pol
-
-    if not args.no_mxfp8 and w.dtype == synth.BF16:
-        wm = w.with_(dtype=synth.MXFP8)
-        m = SparseModel(wm, inputs, layers, dev, waves, streams=S)
-        s_m, _ = time_decodes(m, args.steps, args.warmup, dev)
-        b = sum(sparse_bytes_per_head_step(wm, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
-        result["mxfp8_kv"] = {"value": head_steps / s_m, "unit": "head-steps/s", "ms_per_step": s_m * 1e3,
-                              "hbm_gbs": b / s_m / 1e9, "speedup_vs_bf16_kv": sec / s_m,
-                              "traffic_per_launch": traffic_for(w.name + "_mxfp8", S),
-                              "algorithmic_bytes_per_launch": b / (w.L_dec * layers * S),
-                              "byte_ratio": total_bytes / b, "workspace_gb": m.nbytes * S * layers / 1e9,
-                              "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
-        log("mxfp8 kv: %.1f ms per decode, %.0f GB/s, %.2fx the bf16 cache" % (s_m * 1e3, b / s_m / 1e9, sec / s_m))
-        del m
-
-    if args.profile_dist > 0:
-        result["characterization"] = characterize(w, inputs, dev, args.profile_dist)
-
-    if args.sweep:
-        sweep = []
-        for sp in (0.0, 0.5, 0.8, 0.9, 0.95):
-            n_att = synth.n_att_for(w.L_dec, sp)
-            n_r = w.N_r if n_att <= w.N_r else w.L_dec
-            ws = w.with_(N_att=n_att, N_r=n_r)
-            m = SparseModel(ws, inputs, layers, dev, args.waves, streams=S)
-            s, _ = time_decodes(m, 1, 1, dev)
-            b = sum(sparse_bytes_per_head_step(ws, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
-            sweep.append({"sparsity": sp, "N_r": n_r, "N_att": n_att, "value": head_steps / s,
-                          "hbm_gbs": b / s / 1e9})
-            log("sweep %.2f: %.1f ms" % (sp, s * 1e3))
-            del m
-        result["sweep"] = sweep
-
-    if not args.no_ceiling:
-        c = hbm_read_ceiling(dev)
-        result["hbm_read_ceiling"] = {
-            "kernel": "dsa_hbm_read_probe (16-byte non-temporal loads, grid-stride, 4 GiB, best launch shape)",
-            "GBs": c["GBs"], "frac_of_peak": c["GBs"] / HBM_PEAK_GBS,
-            "shape": {k: c[k] for k in ("blocks", "threads", "unroll")},
-            "sparse_one_stream_frac_of_ceiling": achieved / c["GBs"],
-            "sparse_micro_batched_frac_of_ceiling": (total_bytes / sec_ev / 1e9) / c["GBs"] if S > 1 else None}
-        log("hbm read ceiling: %.0f GB/s (%s)" % (c["GBs"], result["hbm_read_ceiling"]["shape"]))
-
-    if args.cpu_seconds > 0:
-        log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
-
+    res.pop("steps")
+    res.pop("warmup")
+    result.update(res)
+    result["legs"] = legs
+    result["bench_seconds"] = time.perf_counter() - t_start
+    assert layers == result["config"]["layers"]
     print(json.dumps(result), flush=True)
 
 
