@@ -16,6 +16,7 @@ from .binding import (
     DSA_POLICY_SLIDING_WINDOW,
     DSA_POLICY_STREAMING_LLM,
     DSA_POLICY_TOVA,
+    DSA_PROFILE_STATIC_SCRATCH_BYTES,
     DsaError,
     State,
     dense_append_decode_step,
@@ -28,6 +29,7 @@ from .binding import (
     dsa_append_kv,
     dsa_append_prompt,
     dsa_attention_profile,
+    dsa_attention_profile_static,
     dsa_hbm_read_probe,
     dsa_decode_step,
     dsa_last_error,

@@ -41,6 +41,7 @@ _SIGNATURES = {
     "dense_append_decode_step": (_c_int, [_P, _P, _P, _P, _P]),
     "dsa_profile_workspace_bytes": (_c_size, [_c_int] * 5),
     "dsa_attention_profile": (_c_int, [_P, _P, _P] + [_c_int] * 7 + [_P, _c_size, _P, _P, _P, _P]),
+    "dsa_attention_profile_static": (_c_int, [_P, _P, _P] + [_c_int] * 7 + [_P, _P, _P, _P]),
     "dsa_hbm_read_probe": (_c_int, [_P, _c_size, _c_int, _c_int, _c_int, _P, _P]),
     "dsa_set_waves": (_c_int, [_P, _c_int]),
     "dsa_set_splits": (_c_int, [_P, _c_int]),
@@ -227,6 +228,16 @@ def dsa_attention_profile(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_
     return _check(library().dsa_attention_profile(_ptr(q), _ptr(k), _ptr(k_p), batch, heads, head_dim, L_p, T, dtype,
                                                   max_dist, _ptr(workspace), workspace_bytes, _ptr(mass), _ptr(vert),
                                                   _ptr(diag), _stream(stream)))
+
+
+DSA_PROFILE_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def dsa_attention_profile_static(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, mass, vert, diag,
+                                 stream=None):
+    return _check(library().dsa_attention_profile_static(_ptr(q), _ptr(k), _ptr(k_p), batch, heads, head_dim, L_p, T,
+                                                         dtype, max_dist, _ptr(mass), _ptr(vert), _ptr(diag),
+                                                         _stream(stream)))
 
 
 def dsa_hbm_read_probe(src, nbytes, blocks, threads, unroll, sink, stream=None):

@@ -674,9 +674,13 @@ size_t dsa_profile_workspace_bytes(int batch, int heads, int L_p, int T, int max
            align_up(lanes * (size_t)((T + 15) / 16) * 2 * (size_t)max_dist * sizeof(double));
 }
 
-int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
-                          int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
-                          double* vert, double* diag, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both profile entry points (workspace excluded).
+int check_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p, int T,
+                  int dtype, int max_dist, const double* mass, const double* vert, const double* diag) {
     int rc = check_common(batch, L_p, heads, head_dim, dtype);
     if (rc) return rc;
     if (dtype == DSA_MXFP8) return fail(DSA_E_INVAL, "the profile takes fp32 or bf16 inputs");
@@ -691,16 +695,21 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
     if (!mass || !vert || !diag) return fail(DSA_E_INVAL, "an output pointer is NULL");
     if (((uintptr_t)mass | (uintptr_t)vert | (uintptr_t)diag) & 7u)
         return fail(DSA_E_INVAL, "outputs must be 8-byte aligned");
-    rc = check_workspace(d_workspace, workspace_bytes, dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist));
-    if (rc) return rc;
+    return 0;
+}
+
+// The three profile kernels over a checked, large enough workspace.
+int launch_profile_on(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
+                      int T, int dtype, int max_dist, char* ws, double* mass, double* vert, double* diag,
+                      hipStream_t stream) {
+    const long long lanes = (long long)batch * heads;
     dsa::ProfileArgs a;
     a.q = q;
     a.k = k;
     a.k_p = k_p;
-    a.P = static_cast<float*>(d_workspace);
-    a.mass_rows = reinterpret_cast<float*>(static_cast<char*>(d_workspace) + profile_map_bytes(lanes, T));
-    a.partial = reinterpret_cast<double*>(static_cast<char*>(d_workspace) + profile_map_bytes(lanes, T) +
-                                          profile_mass_bytes(lanes, T));
+    a.P = reinterpret_cast<float*>(ws);
+    a.mass_rows = reinterpret_cast<float*>(ws + profile_map_bytes(lanes, T));
+    a.partial = reinterpret_cast<double*>(ws + profile_map_bytes(lanes, T) + profile_mass_bytes(lanes, T));
     a.mass = mass;
     a.vert = vert;
     a.diag = diag;
@@ -710,9 +719,40 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
     a.L_p = L_p;
     a.T = T;
     a.max_dist = max_dist;
-    hipError_t e = dsa::launch_profile(dtype, head_dim, a, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = dsa::launch_profile(dtype, head_dim, a, stream);
     if (e != hipSuccess) return hip_fail(e, "profile launch");
     return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_attention_profile(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim, int L_p,
+                          int T, int dtype, int max_dist, void* d_workspace, size_t workspace_bytes, double* mass,
+                          double* vert, double* diag, void* hip_stream) {
+    int rc = check_profile(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, mass, vert, diag);
+    if (rc) return rc;
+    rc = check_workspace(d_workspace, workspace_bytes, dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist));
+    if (rc) return rc;
+    return launch_profile_on(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist,
+                             static_cast<char*>(d_workspace), mass, vert, diag, static_cast<hipStream_t>(hip_stream));
+}
+
+int dsa_attention_profile_static(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim,
+                                 int L_p, int T, int dtype, int max_dist, double* mass, double* vert, double* diag,
+                                 void* hip_stream) {
+    int rc = check_profile(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, mass, vert, diag);
+    if (rc) return rc;
+    const size_t need = dsa_profile_workspace_bytes(batch, heads, L_p, T, max_dist);
+    if (need > (size_t)DSA_PROFILE_STATIC_SCRATCH_BYTES)
+        return fail(DSA_E_WORKSPACE, "this profile needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use dsa_attention_profile with a workspace)", need, (size_t)DSA_PROFILE_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    hipError_t e = dsa::profile_static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "static profile scratch address");
+    return launch_profile_on(q, k, k_p, batch, heads, head_dim, L_p, T, dtype, max_dist, static_cast<char*>(ws), mass,
+                             vert, diag, static_cast<hipStream_t>(hip_stream));
 }
 
 int dsa_hbm_read_probe(const void* src, size_t bytes, int blocks, int threads, int unroll, uint32_t* sink,

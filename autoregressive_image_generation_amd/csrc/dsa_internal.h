@@ -104,6 +104,10 @@ constexpr int kMaxProfileDist = 256;  // per-distance sums of a row tile live in
 
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_profile(int dtype, int D, const ProfileArgs& a, hipStream_t s);
+// Device address, on the current device, of the library's static profile
+// scratch (DSA_PROFILE_STATIC_SCRATCH_BYTES bytes, 256-byte aligned); looked
+// up once per device.
+hipError_t profile_static_scratch(void** ptr);
 hipError_t launch_prompt(int dtype, int D, const PromptArgs& a, hipStream_t s);
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, int blocks, int threads, int unroll, uint32_t* sink,
                                  hipStream_t s);

@@ -38,6 +38,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "../../include/dsa.h"
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -593,6 +596,34 @@ hipError_t launch_profile_t(const ProfileArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Scratch of dsa_attention_profile_static: the map, the per-query mass and
+// the per-tile sums of a profile, in device memory the library itself holds
+// (each GPU the library runs on keeps its own copy until the process ends),
+// for callers that cannot allocate a workspace.  Host code never passes this
+// name to a kernel: its device address comes from hipGetSymbolAddress, once
+// per device, below.
+static __device__ __align__(256) char scratch[DSA_PROFILE_STATIC_SCRATCH_BYTES];
+
+hipError_t profile_static_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_profile(int dtype, int D, const ProfileArgs& a, hipStream_t s) {
     if (dtype == 1) return D == 128 ? launch_profile_t<uint16_t, 128>(a, s) : launch_profile_t<uint16_t, 64>(a, s);

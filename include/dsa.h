@@ -284,6 +284,27 @@ int dsa_attention_profile(const void* q, const void* k, const void* k_p, int bat
                           double* vert, double* diag, void* hip_stream);
 
 /*
+ * dsa_attention_profile without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * outputs, with the scratch (the map, the per-query mass and the per-tile
+ * sums, dsa_profile_workspace_bytes(...) bytes) taken from a static device
+ * array of DSA_PROFILE_STATIC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends.  A profile that needs more scratch
+ * fails with DSA_E_WORKSPACE and launches nothing (64 MiB holds, e.g., one
+ * sequence of 32 heads over 576 decode steps).  The call allocates nothing;
+ * its first call on a device looks up that device's copy of the array (the
+ * stream must belong to the current device).  Every call on one GPU shares
+ * that GPU's copy: calls that overlap on one GPU (several streams, or several
+ * host threads) race on it and must be serialised by the caller; one stream
+ * orders them by itself.  No part of the scratch needs to start at zero.
+ */
+#define DSA_PROFILE_STATIC_SCRATCH_BYTES (64u << 20)
+int dsa_attention_profile_static(const void* q, const void* k, const void* k_p, int batch, int heads, int head_dim,
+                                 int L_p, int T, int dtype, int max_dist, double* mass, double* vert, double* diag,
+                                 void* hip_stream);
+
+/*
  * HBM read probe (a measurement utility, not part of the method): streams
  * `bytes` from src once with 16-byte non-temporal loads, grid-stride over
  * `blocks` workgroups of `threads`, `unroll` loads in flight per thread, the

@@ -20,6 +20,7 @@ FAKE_WS = 1 << 40  # an aligned address that is never dereferenced by these test
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^#.*$", "", text, flags=re.M)  # preprocessor lines (a #define with parentheses)
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"})
 
 

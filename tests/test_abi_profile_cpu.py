@@ -72,3 +72,21 @@ def test_read_probe_rejects_bad_arguments_before_launch(kw):
     with pytest.raises(DsaError) as e:
         _probe(**kw)
     assert e.value.code == -1
+
+
+def test_static_profile_rejects_before_launch():
+    """The allocation-free profile checks its arguments like the workspace one
+    and refuses a profile whose scratch exceeds the static array, on the host
+    (nothing is launched: no GPU is needed)."""
+    fake = 1 << 40
+    lim = dsa.DSA_PROFILE_STATIC_SCRATCH_BYTES
+    lib = dsa.library()
+    # 96 x 32 lanes of 576 x 576 fp32 maps: far beyond the array
+    assert dsa.dsa_profile_workspace_bytes(96, 32, 64, 576, 48) > lim
+    assert lib.dsa_attention_profile_static(fake, fake, fake, 96, 32, 128, 64, 576, 1, 48, fake, fake, fake,
+                                            None) == -3
+    assert "static scratch" in dsa.dsa_last_error()
+    # the argument checks come first
+    assert lib.dsa_attention_profile_static(fake, fake, fake, 1, 4, 96, 16, 64, 0, 8, fake, fake, fake, None) == -1
+    assert lib.dsa_attention_profile_static(fake, fake, fake, 1, 4, 64, 16, 64, 0, 64, fake, fake, fake, None) == -1
+    assert lib.dsa_attention_profile_static(None, fake, fake, 1, 4, 64, 16, 64, 0, 8, fake, fake, fake, None) == -1
