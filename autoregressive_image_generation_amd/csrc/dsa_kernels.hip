@@ -156,27 +156,63 @@ struct Mx8 {
     };
 };
 
-// Exchange a double with the lane a DPP pattern names (both halves moved).
+// The value of the lane a DPP pattern names.  Every pattern used here names
+// a lane inside the same row of 16 for every lane, so no lane reads out of
+// bounds and the moves need no fill value.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
-    int lo = __double2loint(v);
-    int hi = __double2hiint(v);
-    lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
-    hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
     return __hiloint2double(hi, lo);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the TPR consecutive lanes of a thread group; every lane of the
 // group ends with the same bits (each step adds a value and its partner's,
 // and IEEE addition is commutative).
-template <int TPR>
-__device__ __forceinline__ double group_sum(double v) {
-    v += dpp_f64<0xB1>(v);                            // quad_perm [1,0,3,2]
-    v += dpp_f64<0x4E>(v);                            // quad_perm [2,3,0,1]
-    if constexpr (TPR >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
-    if constexpr (TPR >= 16) v += dpp_f64<0x140>(v);  // row_mirror
+template <int TPR, typename V>
+__device__ __forceinline__ V group_sum(V v) {
+    if constexpr (sizeof(V) == 8) {
+        v += dpp_f64<0xB1>(v);                            // quad_perm [1,0,3,2]
+        v += dpp_f64<0x4E>(v);                            // quad_perm [2,3,0,1]
+        if constexpr (TPR >= 8) v += dpp_f64<0x141>(v);   // row_half_mirror
+        if constexpr (TPR >= 16) v += dpp_f64<0x140>(v);  // row_mirror
+    } else {
+        v += dpp_f32<0xB1>(v);
+        v += dpp_f32<0x4E>(v);
+        if constexpr (TPR >= 8) v += dpp_f32<0x141>(v);
+        if constexpr (TPR >= 16) v += dpp_f32<0x140>(v);
+    }
     if constexpr (TPR >= 32) v += __shfl_xor(v, 16);
     return v;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// q . k over a thread's 8 bf16 elements in fp32 (v_dot2_f32_bf16: two
+// products per instruction, accumulated in fp32).
+__device__ __forceinline__ float dot8_bf16(const uint4& q, const uint4& k) {
+    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), 0.0f,
+                                              false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), p, false);
+    return p;
+}
+
+// Clamp the 8 int16 offsets of a list chunk into [0, hi].
+__device__ __forceinline__ uint4 clamp_offsets(uint4 c, int hi) {
+    uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int a = min(max((int)(int16_t)(w[i] & 0xffffu), 0), hi);
+        const int b = min(max((int)(int16_t)(w[i] >> 16), 0), hi);
+        w[i] = (uint32_t)a | ((uint32_t)b << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Maximum over the 4 lanes of a quad (every lane ends with it).
@@ -327,9 +363,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         long long sidx;  // MXFP8: the row's index among the lane's scale words
         d = -1;
         if constexpr (MODE == MODE_SPARSE) {
-            // Offsets are written only by this kernel and lie in [0, N_rw);
-            // the clamp keeps a damaged workspace from turning into stray reads.
-            const int dl = min(max((int)s_list[max(r - win0, 0)], 0), a.N_rw - 1);
+            const int dl = s_list[max(r - win0, 0)];  // clamped into [0, N_rw) when staged
             int slot = a.base - dl;
             slot += slot < 0 ? a.N_rw : 0;
             // the current token is a listed entry (offset 0) or, while t < S, a sink
@@ -402,9 +436,14 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         if constexpr (MX && MODE == MODE_SPARSE) {
             if (tid == 0) s_self_j = -1;
         }
-        if (tid < nch) s_dyn16[tid] = lc0;
-        if (tid + (int)blockDim.x < nch) s_dyn16[tid + blockDim.x] = lc1;
-        for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_dyn16[c] = load16(idx16 + c);
+        // Sparse offsets are written only by this kernel and lie in [0, N_rw);
+        // they are clamped once here so that a damaged workspace cannot turn
+        // into stray reads.  The slot metadata of TOVA / H2O is clamped where
+        // it is used.
+        auto stage = [&](uint4 c) { return MODE == MODE_SPARSE ? clamp_offsets(c, a.N_rw - 1) : c; };
+        if (tid < nch) s_dyn16[tid] = stage(lc0);
+        if (tid + (int)blockDim.x < nch) s_dyn16[tid + blockDim.x] = stage(lc1);
+        for (int c = tid + 2 * (int)blockDim.x; c < nch; c += blockDim.x) s_dyn16[c] = stage(load16(idx16 + c));
         __syncthreads();
     }
     if constexpr (SLOTS) {
@@ -429,16 +468,35 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     double best_s = __builtin_inf();
     int best_d = -1, best_j = -1;
 
-    // Consume one row: logit in fp64, argmin candidate, online softmax.  Rows
-    // past this group's share (k >= nk), and the out-of-stream current token
-    // of MXFP8, enter with logit -inf and weight 0: selects instead of
-    // branches, so the loop below stays straight-line.
+    // Logits the argmin reads (the window rows of a selection step: the
+    // argmin candidates of Algorithm 1 and TOVA) and all of H2O's rows (its
+    // scores are fp64 probabilities) are exact fp64 dot products.  The other
+    // rows of bf16 caches feed only the softmax and take an fp32 dot product
+    // of the bf16 pairs (v_dot2_f32_bf16).  The choice is made per wavefront
+    // and iteration (uniform), from the wavefront's last row of the iteration.
+    constexpr bool FAST = !MX && sizeof(T) == 2 && MODE != MODE_H2O;
+    const float scale_f = (float)a.scale_log2e;
+
+    // Consume one row: logit, argmin candidate, online softmax.  Rows past
+    // this group's share (k >= nk), and the out-of-stream current token of
+    // MXFP8, enter with logit -inf and weight 0: selects instead of branches,
+    // so the loop below stays straight-line apart from the uniform choice of
+    // the logit's precision.
     auto consume = [&](int k, const typename F::Chunk& ch, int d) {
         const int r = r0 + g + k * G;
         int jj = r - win0;  // sparse: list index; TOVA: the slot (below)
         if constexpr (MODE == MODE_TOVA) jj = jj == a.n_occ ? fslot : jj + (jj >= fslot ? 1 : 0);
         float kf[EPT], vf[EPT];
         bool valid = k < nk;
+        float x = -__builtin_inff();  // the logit in log2 units, scaled by 1 / sqrt(D)
+        const bool exact = !FAST || ((MODE == MODE_SPARSE || MODE == MODE_TOVA) && a.select &&
+                                     r0 + wave * GPW + GPW - 1 + k * G >= win0);
+        if constexpr (FAST) {
+            if (!exact) {
+                const float s32 = group_sum<TPR>(dot8_bf16(qx[0], ch.k));
+                x = valid ? s32 * scale_f : -__builtin_inff();
+            }
+        }
         double kscale = 1.0;
         float vscale = 1.0f;
         if constexpr (MX) {
@@ -458,24 +516,26 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             kscale = (double)e8m0_value(ch.s.x >> (8 * b) & 0xffu);
             vscale = e8m0_value(ch.s.y >> (8 * b) & 0xffu);
         } else {
-            unpack<T>(ch.k, kf);
             unpack<T>(ch.v, vf);
         }
-        double part = 0.0;
+        if (exact) {
+            if constexpr (!MX) unpack<T>(ch.k, kf);
+            double part = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
-        if constexpr (MX) part *= kscale;  // a power of two: exact
-        const double s = group_sum<TPR>(part);
-        if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
-            const bool cand = valid && a.select && d >= 0 && better(s, d, best_s, best_d);
-            best_s = cand ? s : best_s;
-            best_d = cand ? d : best_d;
-            best_j = cand ? jj : best_j;
+            for (int e = 0; e < EPT; ++e) part = fma(qd[e], (double)kf[e], part);
+            if constexpr (MX) part *= kscale;  // a power of two: exact
+            const double s = group_sum<TPR>(part);
+            if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
+                const bool cand = valid && a.select && d >= 0 && better(s, d, best_s, best_d);
+                best_s = cand ? s : best_s;
+                best_d = cand ? d : best_d;
+                best_j = cand ? jj : best_j;
+            }
+            if constexpr (MODE == MODE_H2O) {
+                if (valid && sl == 0) s_logit[r] = s;
+            }
+            x = valid ? (float)(s * a.scale_log2e) : -__builtin_inff();
         }
-        if constexpr (MODE == MODE_H2O) {
-            if (valid && sl == 0) s_logit[r] = s;
-        }
-        const float x = valid ? (float)(s * a.scale_log2e) : -__builtin_inff();
         if constexpr (MX) {
             // 16 accumulators per thread: the running maximum moves only when
             // a logit exceeds it by more than 8 (log2 units), so weights stay
