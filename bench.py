@@ -44,14 +44,14 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 # profiles/ summaries give the commands.  Keyed by workload and tied to the
 # kernel source it was measured on: reported as null once that source changes.
 TRAFFIC = {
-    # batch 96 on one stream: decode dispatches 12000-12299 (steps 400-409, phase 3),
-    # algorithmic bytes of the same launches 150386688
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.76e6, "kernel_sha256_16": "95d0d8a1116d6233"},
-    # two micro-batches of 48: dispatches 24000-24599 (the same steps), algorithmic 75193344
-    ("janus_pro_7b", 2): {"bytes_per_launch": 75.46e6, "kernel_sha256_16": "95d0d8a1116d6233"},
-    # MXFP8 cache, two micro-batches of 48: dispatches 24000-24599 of its own decode kernel
-    # (steps 400-409), algorithmic 39.39 MB; a window row's scale word comes with a 64-byte segment
-    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.85e6, "kernel_sha256_16": "95d0d8a1116d6233"},
+    # one stream, dispatches 12480-12779 (steps 400-409, phase 3); algorithmic bytes of the same launches 150386688 (phase 2 window: counters / algorithmic 1.0032)
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "algorithmic_bytes_per_launch": 150386688, "kernel_sha256_16": "5e737f044dc6fc4e"},
+    # one stream, dispatches 9984-10283 (steps 400-412, phase 3); algorithmic bytes of the same launches 32696320 (phase 2 window: counters / algorithmic 1.0073)
+    ("janus_pro_1b", 1): {"bytes_per_launch": 32.92e6, "algorithmic_bytes_per_launch": 32696320, "kernel_sha256_16": "5e737f044dc6fc4e"},
+    # one stream, dispatches 96512-96811 (steps 3000-3009, phase 3); algorithmic bytes of the same launches 79770624 (phase 2 window: counters / algorithmic 1.0039)
+    ("lumina_mgpt_7b_1024", 1): {"bytes_per_launch": 80.06e6, "algorithmic_bytes_per_launch": 79770624, "kernel_sha256_16": "5e737f044dc6fc4e"},
+    # one stream, dispatches 192512-192811 (steps 6000-6009, phase 3); algorithmic bytes of the same launches 119491584 (phase 2 window: counters / algorithmic 1.0025)
+    ("hires_8100_sink4", 1): {"bytes_per_launch": 119.8e6, "algorithmic_bytes_per_launch": 119491584, "kernel_sha256_16": "5e737f044dc6fc4e"},
 }
 
 LEG_WORKLOADS = "janus_pro_1b,lumina_mgpt_7b_1024,hires_8100_sink4"
@@ -65,11 +65,14 @@ def kernel_sha16():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(name, streams=1):
+def traffic_for(name, streams=1, ratio=False):
+    """Counter bytes per launch of the workload's counter window (or, with
+    ratio, their quotient by the algorithmic bytes of the same launches);
+    None when not measured for the current kernel source."""
     t = TRAFFIC.get((name, streams))
     if not t or t["kernel_sha256_16"] != kernel_sha16():
         return None
-    return t["bytes_per_launch"]
+    return t["bytes_per_launch"] / t["algorithmic_bytes_per_launch"] if ratio else t["bytes_per_launch"]
 
 
 def parse():
@@ -757,6 +760,7 @@ def measure_workload(w, dev, args, headline):
         "hbm_gbs": total_bytes / sec / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(w.name),
+                     "traffic_over_algorithmic": traffic_for(w.name, ratio=True),
                      "kernel": "decode_kernel (sparse), whole batch per launch, one stream",
                      "avg_launch_us": launch_s * 1e6,
                      "bytes_per_launch": bytes_per_launch,
