@@ -203,6 +203,23 @@ __device__ __forceinline__ float dot8_bf16(const uint4& q, const uint4& k) {
     return p;
 }
 
+// The same for 16 bf16 q elements (two chunks) and 16 E4M3 codes, unscaled:
+// each pair of codes widens exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1; every E4M3 value is a bf16 value), then v_dot2_f32_bf16.
+__device__ __forceinline__ float dot16_bf16_e4m3(const uint4& q0, const uint4& q1, const uint4& k) {
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, true);
+        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[2 * i]), lo, p, false);
+        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[2 * i + 1]), hi, p, false);
+    }
+    return p;
+}
+
 // Clamp the 8 int16 offsets of a list chunk into [0, hi].
 __device__ __forceinline__ uint4 clamp_offsets(uint4 c, int hi) {
     uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -471,10 +488,14 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     // Logits the argmin reads (the window rows of a selection step: the
     // argmin candidates of Algorithm 1 and TOVA) and all of H2O's rows (its
     // scores are fp64 probabilities) are exact fp64 dot products.  The other
-    // rows of bf16 caches feed only the softmax and take an fp32 dot product
-    // of the bf16 pairs (v_dot2_f32_bf16).  The choice is made per wavefront
-    // and iteration (uniform), from the wavefront's last row of the iteration.
-    constexpr bool FAST = !MX && sizeof(T) == 2 && MODE != MODE_H2O;
+    // rows of bf16 and MXFP8 caches feed only the softmax and take an fp32
+    // dot product of bf16 pairs (v_dot2_f32_bf16; MXFP8 codes widened to
+    // bf16 first, the block scale applied to the sum).  The choice is made
+    // per wavefront and iteration (uniform), from the wavefront's last row of
+    // the iteration.  MXFP8 takes it at pipeline depth 3 only: at depth 4 the
+    // two paths together need more registers than 3 wavefronts per SIMD
+    // leave (measured slower).
+    constexpr bool FAST = sizeof(T) == 2 && MODE != MODE_H2O && (!MX || U <= 3);
     const float scale_f = (float)a.scale_log2e;
 
     // Consume one row: logit, argmin candidate, online softmax.  Rows past
@@ -491,7 +512,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         float x = -__builtin_inff();  // the logit in log2 units, scaled by 1 / sqrt(D)
         const bool exact = !FAST || ((MODE == MODE_SPARSE || MODE == MODE_TOVA) && a.select &&
                                      r0 + wave * GPW + GPW - 1 + k * G >= win0);
-        if constexpr (FAST) {
+        if constexpr (FAST && !MX) {
             if (!exact) {
                 const float s32 = group_sum<TPR>(dot8_bf16(qx[0], ch.k));
                 x = valid ? s32 * scale_f : -__builtin_inff();
@@ -510,11 +531,23 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             // row past the group's share) enters with weight 0.  Every cache
             // row holds zeros (cleared at state init) or the quantiser's codes
             // (no NaN code, scale bytes below 0xFF), so 0 times its values is 0.
-            unpack_e4m3(ch.k, kf);
             unpack_e4m3(ch.v, vf);
             const int b = sl * EPT / 32;  // this thread's elements lie in block b of 32
-            kscale = (double)e8m0_value(ch.s.x >> (8 * b) & 0xffu);
+            const float kscale_f = e8m0_value(ch.s.x >> (8 * b) & 0xffu);
+            kscale = (double)kscale_f;
             vscale = e8m0_value(ch.s.y >> (8 * b) & 0xffu);
+            if constexpr (FAST) {
+                if (exact) {
+                    unpack_e4m3(ch.k, kf);
+                } else {
+                    // the block scale is a power of two: scaling each thread's
+                    // partial sum before the group sum is exact
+                    const float s32 = group_sum<TPR>(dot16_bf16_e4m3(qx[0], qx[1], ch.k) * kscale_f);
+                    x = valid ? s32 * scale_f : -__builtin_inff();
+                }
+            } else {
+                unpack_e4m3(ch.k, kf);
+            }
         } else {
             unpack<T>(ch.v, vf);
         }
