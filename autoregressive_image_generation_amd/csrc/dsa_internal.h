@@ -92,7 +92,7 @@ struct ProfileArgs {
     const void* q;         // [T][B][H][D] decode queries
     const void* k;         // [T][B][H][D] decode keys
     const void* k_p;       // [B][L_p][H][D] prompt keys
-    float* P;              // workspace: [lanes][T][T] decode probabilities (j <= i written)
+    float* P;              // workspace: [lanes][T][T] decode weights, each row its probabilities times a row constant (j <= i written)
     float* mass_rows;      // workspace: [lanes][T][3] prompt / local / middle mass per query
     double* mass;          // out: [lanes][3] mean over queries
     double* vert;          // out: [lanes][max_dist] mean vertical cosine similarity, distance 1..max_dist

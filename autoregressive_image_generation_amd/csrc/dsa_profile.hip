@@ -8,10 +8,12 @@
 // workgroup sharing each 16-key tile through LDS.  The logits Q K^T are a
 // dense contraction, computed in 16 x 16 tiles with MFMA (bf16:
 // v_mfma_f32_16x16x16_bf16, fp32: v_mfma_f32_16x16x4_f32; fp32 sums), the
-// query operand held in registers.  Pass 1 keeps each lane's online
-// (max, sum) over its key columns and merges the 16 lanes of a query once;
-// pass 2 recomputes the tiles, writes the decode probabilities P[i][j]
-// (j <= i) and the per-query mass split.
+// query operand held in registers.  Pass 1 takes each query's maximum logit
+// m over its key columns; pass 2 recomputes the tiles and writes the decode
+// weights P[i][j] = 2^(x - m) (j <= i; x the logit in base 2): each row is
+// the row of probabilities times the row's softmax sum, which leaves every
+// cosine below unchanged.  The mass split divides each key group's sum of
+// weights by the row's total.
 //
 // profile_gram_kernel: every similarity term is a band of a Gram matrix.
 // With Q[i][o] = P[i][i - o] (the map in offset coordinates: o = i - j),
@@ -67,15 +69,6 @@ struct MfmaIn<float> {  // fp32: 4 dimensions per step, 1 per lane
     __device__ static Op load(const float* p) { return *p; }
     __device__ static f32x4 mfma(Op a, Op b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
 };
-
-// Merge two base-2 online-softmax states (max, sum); -inf max = empty.
-__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
-    const float mn = fmaxf(m, m2);
-    const float a = m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f(m - mn);
-    const float b = m2 == -INFINITY ? 0.0f : s2 * __builtin_amdgcn_exp2f(m2 - mn);
-    m = mn;
-    s = a + b;
-}
 
 __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
@@ -146,10 +139,16 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     using M = MfmaIn<T>;
     constexpr int NS = D / M::STEP;
     constexpr int RSTR = KeyStage<T, D>::RSTR;      // LDS row stride in 8-byte units
+    // blockIdx -> (lane, query tile) with all query tiles of a lane on one
+    // XCD (workgroup x runs on XCD x % 8; lanes are padded to a multiple of
+    // 8): the tiles read overlapping key ranges, from one L2.
     const int tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
-    const int lane = blockIdx.x / tiles;
+    const int x = blockIdx.x;
+    const int lane = (x % 8) + 8 * (x / (8 * tiles));
+    const int tile = (x / 8) % tiles;
+    if (lane >= a.lanes) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: scalar branches below
-    const int i0 = (blockIdx.x % tiles) * 16 * kMapWaves + 16 * wave;  // this wavefront's first query
+    const int i0 = tile * 16 * kMapWaves + 16 * wave;  // this wavefront's first query
     const int l = threadIdx.x % 64;
     const int col = l % 16, quarter = l / 16;
     const int b = lane / a.H, h = lane % a.H;
@@ -165,7 +164,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
 #pragma unroll
         for (int s = 0; s < NS; ++s) qa[s] = M::load(qrow + s * M::STEP);
     }
-    const int ncols = a.L_p + min((blockIdx.x % tiles) * 16 * kMapWaves + 16 * kMapWaves, a.T);  // keys of the group
+    const int ncols = a.L_p + min(tile * 16 * kMapWaves + 16 * kMapWaves, a.T);  // keys of the group
     // (the stage is used directly, not through lambdas: captured by
     // reference, its registers would be demoted to scratch memory)
     KeyStage<T, D> pf;
@@ -175,14 +174,11 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     const int first_key = i0 + 15 < a.T ? min(a.L_p + i0, ncols - 1) : -1;
     const int last_key = a.L_p + min(i0 + 15, a.T - 1);
 
-    // pass 1: this lane's online (max, sum) per query over its columns, then
-    // the 16 lanes of each query merged
-    float m[4], s[4];
+    // pass 1: the maximum logit of each query over its columns (this lane's,
+    // then the 16 lanes of the query merged)
+    float m[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        m[e] = -INFINITY;
-        s[e] = 0.0f;
-    }
+    for (int e = 0; e < 4; ++e) m[e] = -INFINITY;
     pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
     for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
         __syncthreads();
@@ -203,18 +199,15 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
                 if (cmin >= ncols || cmin > last_key) break;
                 const int c = cmin + col;
                 const f32x4 t = ts[q2];
-                const bool full = cmin + 15 <= first_key;  // every key causal for every query (uniform)
+                if (cmin + 15 <= first_key) {  // every key causal for every query (uniform)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = i0 + 4 * quarter + e;
-                    const bool ok = full || (c < ncols && c <= a.L_p + i);
-                    const float x = t[e] * scale;
-                    const bool need = ok && !(x <= m[e] + 8.0f);
-                    if (__builtin_amdgcn_ballot_w64(need)) {
-                        s[e] *= need ? __builtin_amdgcn_exp2f(m[e] - x) : 1.0f;
-                        m[e] = need ? x : m[e];
+                    for (int e = 0; e < 4; ++e) m[e] = fmaxf(m[e], t[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = c < ncols && c <= a.L_p + i0 + 4 * quarter + e;
+                        m[e] = ok ? fmaxf(m[e], t[e]) : m[e];
                     }
-                    s[e] += ok ? __builtin_amdgcn_exp2f(x - m[e]) : 0.0f;
                 }
             }
         }
@@ -222,15 +215,15 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) merge_ms(m[e], s[e], __shfl_xor(m[e], o), __shfl_xor(s[e], o));
+        for (int o = 1; o < 16; o <<= 1) m[e] = fmaxf(m[e], __shfl_xor(m[e], o));
+        m[e] *= scale;  // scale > 0: the maximum of the scaled logits
     }
 
-    // pass 2: probabilities of the decode keys and the mass split
+    // pass 2: the weights 2^(x - m) of the decode keys (the probabilities up to
+    // the row's normaliser: the cosines do not depend on a row's scale) and
+    // the mass of each key group, divided by the row's total at the end
     float* P = a.P + (size_t)lane * a.T * a.T;
     float mp[4] = {0, 0, 0, 0}, ml[4] = {0, 0, 0, 0}, mm[4] = {0, 0, 0, 0};
-    float inv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) inv[e] = 1.0f / s[e];
     pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
     for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
         __syncthreads();
@@ -258,11 +251,11 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
                 const bool full = cmin + 15 <= first_key;
                 if (full && cmin + 15 < a.L_p) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mp[e] += __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e];
+                    for (int e = 0; e < 4; ++e) mp[e] += __builtin_amdgcn_exp2f(t[e] * scale - m[e]);
                 } else if (full && cmin >= a.L_p && cmin + 15 - a.L_p <= i0 - (i0 + 10) / 10) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e];
+                        const float p = __builtin_amdgcn_exp2f(t[e] * scale - m[e]);
                         mm[e] += p;
                         P[(size_t)(i0 + 4 * quarter + e) * a.T + j] = p;
                     }
@@ -271,7 +264,7 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
                     for (int e = 0; e < 4; ++e) {
                         const int i = i0 + 4 * quarter + e;
                         const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
-                        const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) * inv[e] : 0.0f;
+                        const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) : 0.0f;
                         const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
                         mp[e] += j < 0 ? p : 0.0f;
                         ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
@@ -287,76 +280,113 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
         const int i = i0 + 4 * quarter + e;
         const float vp = sum16(mp[e]), vl = sum16(ml[e]), vm = sum16(mm[e]);
         if (col == 0 && i < a.T) {
+            const float inv = 1.0f / (vp + vl + vm);
             float* r = a.mass_rows + ((size_t)lane * a.T + i) * 3;
-            r[0] = vp;
-            r[1] = vl;
-            r[2] = vm;
+            r[0] = vp * inv;
+            r[1] = vl * inv;
+            r[2] = vm * inv;
         }
     }
 }
 
 constexpr int kGramWaves = 4;  // row tiles per workgroup (one per wavefront)
 constexpr int kGramJ = 4;      // column tiles per pass (accumulators: 4 products x 4 tiles)
-constexpr int kGChunk = 16;    // staged columns per LDS chunk (its prefetch registers still fit 3 waves per SIMD)
-constexpr int kGStride = kGChunk + 1;
-// bf16 row stride of the split copies: 40 bytes, so that the 16 rows of an
-// MFMA operand read (8 bytes each) start in different banks
-constexpr int kGBStride = 20;
+constexpr int kGChunk = 16;    // staged columns per LDS chunk: one bf16 MFMA step
+// A staged row in LDS, per form (P or Q): the chunk's 16 values as four
+// quads of 4 columns, each quad its 4 bf16 hi parts then its 4 bf16 lo parts
+// (one 16-byte read is a lane's operand pair), then 16 bytes of padding, so
+// that the 16 rows of an operand read fall into different banks.
+constexpr int kGRow = 80;  // bytes per staged row and form
 
-// The staged rows in LDS: fp32 (for the norms) and split into bf16 hi / lo
-// (for the Gram products), for P and for Q.
-struct GStage {
-    float *p, *q;
-    uint16_t *ph, *pl, *qh, *ql;
-};
+typedef short bf16x4v __attribute__((ext_vector_type(4)));
+
+// Four fp32 values split into bf16 hi = bf16(x) and lo = bf16(x - hi) (round
+// to nearest even), so x = hi + lo + r with |r| <= 2^-18 |x|: the words
+// (hi0 hi1, hi2 hi3, lo0 lo1, lo2 lo3), element 0 in the low half.
+__device__ __forceinline__ u32x4 split_quad(f32x4 x) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v h01 = {(__bf16)x[0], (__bf16)x[1]};
+    const bf16x2v h23 = {(__bf16)x[2], (__bf16)x[3]};
+    const uint32_t h0 = __builtin_bit_cast(uint32_t, h01), h1 = __builtin_bit_cast(uint32_t, h23);
+    const bf16x2v l01 = {(__bf16)(x[0] - __uint_as_float(h0 << 16)), (__bf16)(x[1] - __uint_as_float(h0 & 0xffff0000u))};
+    const bf16x2v l23 = {(__bf16)(x[2] - __uint_as_float(h1 << 16)), (__bf16)(x[3] - __uint_as_float(h1 & 0xffff0000u))};
+    return u32x4{h0, h1, __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+}
+
+// The hi (words 0, 1) and lo (words 2, 3) halves of a staged quad as MFMA
+// operands.  The halves go through named temporaries: this compiler's
+// __builtin_bit_cast of a swizzle such as w.zw reads w.xy instead.
+__device__ __forceinline__ bf16x4v quad_hi(const u32x4& w) {
+    const u32x2 h = {w[0], w[1]};
+    return __builtin_bit_cast(bf16x4v, h);
+}
+__device__ __forceinline__ bf16x4v quad_lo(const u32x4& w) {
+    const u32x2 l = {w[2], w[3]};
+    return __builtin_bit_cast(bf16x4v, l);
+}
+
+// hi + lo of element e of a staged quad (exact in fp32: both parts are bf16
+// values 8 bits apart at most).
+__device__ __forceinline__ float quad_value(const u32x4& w, int e) {
+    const uint32_t h = e < 2 ? w[0] : w[1], l = e < 2 ? w[2] : w[3];
+    const uint32_t hb = e % 2 ? (h & 0xffff0000u) : (h << 16), lb = e % 2 ? (l & 0xffff0000u) : (l << 16);
+    return __uint_as_float(hb) + __uint_as_float(lb);
+}
+
+// Four consecutive floats at a 4-byte aligned address (one 16-byte load).
+__device__ __forceinline__ f32x4 load_f4(const float* p) {
+    f32x4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
 
 // Columns [k0, k0 + kGChunk) of NROWS rows r0.. of the map, as P (row-major,
 // zero beyond the causal part and past T) and as Q (offset coordinates:
-// Q[r][o] = P[r][r - o], zero for o > r), held in registers: element x of
-// the chunk (row x / kGChunk, column x % kGChunk) is thread x mod 256's
-// entry x / 256, so a wavefront reads two 128-byte row segments per entry.
+// Q[r][o] = P[r][r - o], zero for o > r), held in registers as quads: quad u
+// of the chunk (row u / 4, columns or offsets 4 (u % 4) .. + 3) is thread
+// u mod 256's entry u / 256.  A quad whose four entries are all causal is one
+// 16-byte load (the Q quad reversed), the others are loaded entry by entry.
 template <int NROWS>
 struct Staged {
-    static constexpr int RSTEP = 64 * kGramWaves / kGChunk;  // rows between a thread's entries: 8
-    static constexpr int N = NROWS / RSTEP;
-    static_assert(NROWS % RSTEP == 0 && 64 * kGramWaves % kGChunk == 0, "whole entries per thread");
-    float p[N], q[N];
+    static constexpr int NQ = NROWS * kGChunk / 4;
+    static constexpr int N = (NQ + 64 * kGramWaves - 1) / (64 * kGramWaves);
+    f32x4 p[N], q[N];
 
     // Issue the loads (they complete while the current chunk is consumed).
-    // Thread x holds column kk = x % kGChunk of rows x / kGChunk + RSTEP n.
     __device__ __forceinline__ void load(const float* P, int T, int r0, int k0) {
-        const int rr = threadIdx.x / kGChunk, kx = k0 + threadIdx.x % kGChunk;
-        int r = r0 + rr;
-        const float* pp = P + (size_t)r * T + kx;       // P[r][kx]
-        const float* pq = P + (size_t)r * T + (r - kx);  // P[r][r - kx]
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const bool ok = r < T && kx <= r;
-            p[n] = ok ? *pp : 0.0f;
-            q[n] = ok ? *pq : 0.0f;
-            r += RSTEP;
-            pp += (size_t)RSTEP * T;
-            pq += (size_t)RSTEP * (T + 1);
+            const int u = threadIdx.x + 64 * kGramWaves * n;
+            const int r = r0 + u / 4, c0 = k0 + 4 * (u % 4);
+            p[n] = q[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (u < NQ && r < T) {
+                const float* row = P + (size_t)r * T;
+                if (c0 + 3 <= r) {
+                    p[n] = load_f4(row + c0);
+                    const f32x4 v = load_f4(row + (r - c0 - 3));
+                    q[n] = f32x4{v[3], v[2], v[1], v[0]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (c0 + e <= r) {
+                            p[n][e] = row[c0 + e];
+                            q[n][e] = row[r - c0 - e];
+                        }
+                    }
+                }
+            }
         }
     }
-    __device__ __forceinline__ void store(const GStage& st) const {
-        const int off = (threadIdx.x / kGChunk) * kGStride + threadIdx.x % kGChunk;
-        const int boff = (threadIdx.x / kGChunk) * kGBStride + threadIdx.x % kGChunk;
+    // Store the quads split into bf16 hi / lo: one 16-byte store per form.
+    __device__ __forceinline__ void store(char* sp, char* sq) const {
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            st.p[off + n * RSTEP * kGStride] = p[n];
-            st.q[off + n * RSTEP * kGStride] = q[n];
-            // p and q split together: two packed conversions (round to nearest even)
-            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-            const bf16x2v h2 = {(__bf16)p[n], (__bf16)q[n]};
-            const uint32_t hb = __builtin_bit_cast(uint32_t, h2);
-            const bf16x2v l2 = {(__bf16)(p[n] - __uint_as_float(hb << 16)),
-                                (__bf16)(q[n] - __uint_as_float(hb & 0xffff0000u))};
-            const uint32_t lb = __builtin_bit_cast(uint32_t, l2);
-            st.ph[boff + n * RSTEP * kGBStride] = (uint16_t)hb;
-            st.qh[boff + n * RSTEP * kGBStride] = (uint16_t)(hb >> 16);
-            st.pl[boff + n * RSTEP * kGBStride] = (uint16_t)lb;
-            st.ql[boff + n * RSTEP * kGBStride] = (uint16_t)(lb >> 16);
+            const int u = threadIdx.x + 64 * kGramWaves * n;
+            if (u < NQ) {
+                const int off = (u / 4) * kGRow + (u % 4) * 16;
+                *reinterpret_cast<u32x4*>(sp + off) = split_quad(p[n]);
+                *reinterpret_cast<u32x4*>(sq + off) = split_quad(q[n]);
+            }
         }
     }
 };
@@ -365,7 +395,8 @@ struct Staged {
 // 16 w.  A pass covers the column tiles J = I + 64 g + 16 c (c < 4) of every
 // wavefront: their rows, I0 + 64 g .. I0 + 64 g + 111, are staged once per
 // chunk for all four wavefronts (pass 0 holds the A rows among them; later
-// passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 x 17 floats.
+// passes stage the A rows apart).  Dynamic LDS: (112 [+ 64]) rows x 2 forms x
+// kGRow bytes.
 // MULTI: distances beyond one pass (max_dist > 16 kGramJ - 15): later passes
 // stage the A rows apart.  The one-pass form holds no registers for them and
 // fits three wavefronts per SIMD.
@@ -387,16 +418,12 @@ profile_gram_kernel(ProfileArgs a) {
     const float* P = a.P + (size_t)lane * a.T * a.T;
 
     constexpr int NB = 16 * (kGramWaves + kGramJ - 1);  // B rows of a pass: 112
-    extern __shared__ float s_dyn[];
-    float* sPB = s_dyn;
-    float* sQB = sPB + NB * kGStride;
-    float* sPA = sQB + NB * kGStride;  // later passes only
-    float* sQA = sPA + 16 * kGramWaves * kGStride;
-    constexpr int NA = MULTI ? 16 * kGramWaves : 0;
-    uint16_t* hb = reinterpret_cast<uint16_t*>(s_dyn + 2 * (NB + NA) * kGStride);  // 8-byte aligned
-    const GStage stB{sPB, sQB, hb, hb + NB * kGBStride, hb + 2 * NB * kGBStride, hb + 3 * NB * kGBStride};
-    uint16_t* ha = hb + 4 * NB * kGBStride;
-    const GStage stA{sPA, sQA, ha, ha + NA * kGBStride, ha + 2 * NA * kGBStride, ha + 3 * NA * kGBStride};
+    constexpr int NA = 16 * kGramWaves;  // A rows staged apart (later passes only)
+    extern __shared__ u32x4 s_gram[];    // 16-byte aligned
+    char* const sPB = reinterpret_cast<char*>(s_gram);
+    char* const sQB = sPB + NB * kGRow;
+    char* const sPA = sQB + NB * kGRow;
+    char* const sQA = sPA + NA * kGRow;
     __shared__ double s_sum[2 * kMaxProfileDist];  // per distance: vertical, diagonal
     __shared__ float s_na[16 * kGramWaves];        // |P[i][0..i]|^2 of the block's rows
     for (int d = threadIdx.x; d < 2 * a.max_dist; d += 64 * kGramWaves) s_sum[d] = 0.0;
@@ -414,24 +441,24 @@ profile_gram_kernel(ProfileArgs a) {
             sb[c] = sc[c] = 0.0f;
         }
         const int aoff = 16 * wave;            // this wavefront's A rows in that buffer
-        const GStage& sa = g == 0 ? stB : stA;
+        const char* const saP = g == 0 ? sPB : sPA;
+        const char* const saQ = g == 0 ? sQB : sQA;
         // The chunk's Gram products, all 16 columns in one step per product:
         // bf16 MFMA (16 x 16 x 16) of the split operands, hi.hi + hi.lo + lo.hi.
         // Lane l holds columns 4 (l / 16) .. + 3 of row l % 16 of A and of B.
         auto gram_chunk = [&]() {
-            typedef short bf16x4v __attribute__((ext_vector_type(4)));
-            const int ao = (aoff + col) * kGBStride + 4 * quarter;
-            const bf16x4v pah = *reinterpret_cast<const bf16x4v*>(sa.ph + ao);
-            const bf16x4v pal = *reinterpret_cast<const bf16x4v*>(sa.pl + ao);
-            const bf16x4v qah = *reinterpret_cast<const bf16x4v*>(sa.qh + ao);
-            const bf16x4v qal = *reinterpret_cast<const bf16x4v*>(sa.ql + ao);
+            const int ao = (aoff + col) * kGRow + 16 * quarter;
+            const u32x4 pa = *reinterpret_cast<const u32x4*>(saP + ao);
+            const u32x4 qa = *reinterpret_cast<const u32x4*>(saQ + ao);
+            const bf16x4v pah = quad_hi(pa), pal = quad_lo(pa);
+            const bf16x4v qah = quad_hi(qa), qal = quad_lo(qa);
 #pragma unroll
             for (int c = 0; c < kGramJ; ++c) {
-                const int bo = (16 * (wave + c) + col) * kGBStride + 4 * quarter;
-                const bf16x4v pbh = *reinterpret_cast<const bf16x4v*>(stB.ph + bo);
-                const bf16x4v pbl = *reinterpret_cast<const bf16x4v*>(stB.pl + bo);
-                const bf16x4v qbh = *reinterpret_cast<const bf16x4v*>(stB.qh + bo);
-                const bf16x4v qbl = *reinterpret_cast<const bf16x4v*>(stB.ql + bo);
+                const int bo = (16 * (wave + c) + col) * kGRow + 16 * quarter;
+                const u32x4 pb = *reinterpret_cast<const u32x4*>(sPB + bo);
+                const u32x4 qb = *reinterpret_cast<const u32x4*>(sQB + bo);
+                const bf16x4v pbh = quad_hi(pb), pbl = quad_lo(pb);
+                const bf16x4v qbh = quad_hi(qb), qbl = quad_lo(qb);
                 gv[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, pbh, gv[c], 0, 0, 0);
                 gd[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qah, qbh, gd[c], 0, 0, 0);
                 gv[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, pbl, gv[c], 0, 0, 0);
@@ -448,8 +475,8 @@ profile_gram_kernel(ProfileArgs a) {
         if (MULTI && g > 0) nxA.load(P, a.T, I0, 0);
         for (int k0 = 0; k0 < kend; k0 += kGChunk) {
             __syncthreads();
-            nxB.store(stB);
-            if (MULTI && g > 0) nxA.store(stA);
+            nxB.store(sPB, sQB);
+            if (MULTI && g > 0) nxA.store(sPA, sQA);
             __syncthreads();
             if (k0 + kGChunk < kend) {
                 nxB.load(P, a.T, I0 + 16 * kGramJ * g, k0 + kGChunk);
@@ -458,34 +485,46 @@ profile_gram_kernel(ProfileArgs a) {
             if (I < a.T && k0 + kGChunk - 1 < I) {
                 // every column of the chunk lies left of the tile's first row:
                 // L is 1 for all (i, k), so the prefix norms take plain sums
-                // of squares of the B rows (this lane: columns k = quarter mod 4)
+                // of squares of the B rows (this lane: the quad of columns
+                // 4 quarter .. + 3, as hi + lo)
                 gram_chunk();
-                for (int kk = 0; kk < kGChunk; kk += 4) {
-                    const int kl = kk + quarter;
 #pragma unroll
-                    for (int c = 0; c < kGramJ; ++c) {
-                        const int rb = 16 * (wave + c) + col;
-                        const float pb = sPB[rb * kGStride + kl];
-                        const float qb = sQB[rb * kGStride + kl];
-                        sb[c] = fmaf(pb, pb, sb[c]);
-                        sc[c] = fmaf(qb, qb, sc[c]);
+                for (int c = 0; c < kGramJ; ++c) {
+                    const int bo = (16 * (wave + c) + col) * kGRow + 16 * quarter;
+                    const u32x4 pb = *reinterpret_cast<const u32x4*>(sPB + bo);
+                    const u32x4 qb = *reinterpret_cast<const u32x4*>(sQB + bo);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float xp = quad_value(pb, e), xq = quad_value(qb, e);
+                        sb[c] = fmaf(xp, xp, sb[c]);
+                        sc[c] = fmaf(xq, xq, sc[c]);
                     }
                 }
             } else if (I < a.T && k0 <= I + 15) {  // past I + 15 this wavefront's A rows are zero
                 // A rows are zero past column I + 15, so the Gram step may
                 // run over all 16 columns
+                // (the staged entries past T or past a row's causal part are
+                // zero, so the steps run over all 16 columns)
                 gram_chunk();
-                const int kc = min(kGChunk, kend - k0);
-                for (int kk = 0; kk < kc; kk += 4) {
-                    const int kl = kk + quarter;                               // this lane's column in the step
-                    const float ind = (k0 + kl <= I + col) ? 1.0f : 0.0f;       // L[I + col][k]
+                u32x4 pbq[kGramJ], qbq[kGramJ];  // this lane's quads of the B rows J0 + 16 c + col
+#pragma unroll
+                for (int c = 0; c < kGramJ; ++c) {
+                    const int bo = (16 * (wave + c) + col) * kGRow + 16 * quarter;
+                    pbq[c] = *reinterpret_cast<const u32x4*>(sPB + bo);
+                    qbq[c] = *reinterpret_cast<const u32x4*>(sQB + bo);
+                }
+                // step e: lane (col, quarter) supplies L[I + col][k] and the B
+                // rows' squares at column k = k0 + 4 quarter + e (its k index
+                // is quarter in both operands), so the four steps cover the
+                // chunk's 16 columns once
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ind = (k0 + 4 * quarter + e <= I + col) ? 1.0f : 0.0f;  // L[I + col][k]
 #pragma unroll
                     for (int c = 0; c < kGramJ; ++c) {
-                        const int rb = 16 * (wave + c) + col;                   // B row J0 + 16 c + col
-                        const float pb = sPB[rb * kGStride + kl];
-                        const float qb = sQB[rb * kGStride + kl];
-                        nb[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, pb * pb, nb[c], 0, 0, 0);
-                        nc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, qb * qb, nc[c], 0, 0, 0);
+                        const float xp = quad_value(pbq[c], e), xq = quad_value(qbq[c], e);
+                        nb[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, xp * xp, nb[c], 0, 0, 0);
+                        nc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ind, xq * xq, nc[c], 0, 0, 0);
                     }
                 }
             }
@@ -539,7 +578,7 @@ profile_gram_kernel(ProfileArgs a) {
 size_t gram_lds_bytes(int max_dist) {
     const int passes = (15 + max_dist) / (16 * kGramJ) + 1;
     const int rows = 16 * (kGramWaves + kGramJ - 1) + (passes > 1 ? 16 * kGramWaves : 0);
-    return (size_t)rows * (2 * kGStride * sizeof(float) + 4 * kGBStride * sizeof(uint16_t));
+    return (size_t)rows * 2 * kGRow;
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -576,11 +615,11 @@ template <typename T, int D>
 hipError_t launch_profile_t(const ProfileArgs& a, hipStream_t s) {
     const int tiles = (a.T + 15) / 16;
     const int map_tiles = (a.T + 16 * kMapWaves - 1) / (16 * kMapWaves);
-    hipLaunchKernelGGL((profile_map_kernel<T, D>), dim3((unsigned)((long long)a.lanes * map_tiles)),
-                       dim3(64 * kMapWaves), 0, s, a);
+    const long long lanes8 = ((long long)a.lanes + 7) / 8 * 8;  // both grids: lanes padded to whole XCD rounds
+    hipLaunchKernelGGL((profile_map_kernel<T, D>), dim3((unsigned)(lanes8 * map_tiles)), dim3(64 * kMapWaves), 0, s,
+                       a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long lanes8 = ((long long)a.lanes + 7) / 8 * 8;
     const int blocks = (tiles + kGramWaves - 1) / kGramWaves;
     const bool multi = (15 + a.max_dist) / (16 * kGramJ) + 1 > 1;
     if (multi)
