@@ -15,11 +15,13 @@
 // Single-query decode does about one flop per byte of KV, so the kernel is
 // bound by HBM bandwidth; MFMA has no role.
 //
-// The raw logits q.k are accumulated in fp64: the products of bf16 (or fp32,
-// or MXFP8) values are exact in fp64 and their sums nearly always are, so the
-// argmin decision matches a fp64 reference up to order-of-summation rounding
-// far below the selection's near-tie threshold.  The softmax runs in fp32 on
-// the rounded logits.
+// The raw logits q.k that a selection reads are accumulated in fp64: the
+// products of bf16 (or fp32, or MXFP8) values are exact in fp64 and their sums
+// nearly always are, so the argmin decision matches a fp64 reference up to
+// order-of-summation rounding far below the selection's near-tie threshold.
+// Logits that only the softmax reads take an fp32 dot product of bf16 pairs
+// (bf16 and MXFP8 caches; see consume()).  The softmax runs in fp32 on the
+// rounded logits.
 //
 // Cache row formats:
 //   Plain<T>: K then V, D elements of T each (bf16 bit patterns or fp32); a

@@ -333,6 +333,13 @@ __device__ __forceinline__ float quad_value(const u32x4& w, int e) {
     return __uint_as_float(hb) + __uint_as_float(lb);
 }
 
+// The value of lane CTRL names inside this lane's quad (DPP quad_perm; every
+// lane of the quad is active where it is used).
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 // Four consecutive floats at a 4-byte aligned address (one 16-byte load).
 __device__ __forceinline__ f32x4 load_f4(const float* p) {
     f32x4 v;
@@ -378,14 +385,34 @@ struct Staged {
         }
     }
     // Store the quads split into bf16 hi / lo: one 16-byte store per form.
-    __device__ __forceinline__ void store(char* sp, char* sq) const {
+    // With SQ, also each row's sum of squares over the chunk (fp32, of the
+    // unsplit values), per form: the four quads of a row sit in four
+    // consecutive lanes, which DPP adds.
+    template <bool SQ>
+    __device__ __forceinline__ void store(char* sp, char* sq, float* ssp, float* ssq) const {
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             const int u = threadIdx.x + 64 * kGramWaves * n;
-            if (u < NQ) {
+            if (u < NQ) {  // NQ is a multiple of 4: whole rows, so all four lanes of a quad group take part
                 const int off = (u / 4) * kGRow + (u % 4) * 16;
                 *reinterpret_cast<u32x4*>(sp + off) = split_quad(p[n]);
                 *reinterpret_cast<u32x4*>(sq + off) = split_quad(q[n]);
+                if constexpr (SQ) {
+                    float a = 0.0f, b = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a = fmaf(p[n][e], p[n][e], a);
+                        b = fmaf(q[n][e], q[n][e], b);
+                    }
+                    a += quad_swap<0xB1>(a);  // quad_perm [1,0,3,2]
+                    b += quad_swap<0xB1>(b);
+                    a += quad_swap<0x4E>(a);  // quad_perm [2,3,0,1]
+                    b += quad_swap<0x4E>(b);
+                    if (u % 4 == 0) {
+                        ssp[u / 4] = a;
+                        ssq[u / 4] = b;
+                    }
+                }
             }
         }
     }
@@ -426,6 +453,7 @@ profile_gram_kernel(ProfileArgs a) {
     char* const sQA = sPA + NA * kGRow;
     __shared__ double s_sum[2 * kMaxProfileDist];  // per distance: vertical, diagonal
     __shared__ float s_na[16 * kGramWaves];        // |P[i][0..i]|^2 of the block's rows
+    __shared__ float s_sqP[NB], s_sqQ[NB];         // each B row's sum of squares over the staged chunk
     for (int d = threadIdx.x; d < 2 * a.max_dist; d += 64 * kGramWaves) s_sum[d] = 0.0;
 
     const int kend = min(I0 + 16 * kGramWaves, a.T);                 // P[i][k] = 0 for k > i
@@ -475,8 +503,8 @@ profile_gram_kernel(ProfileArgs a) {
         if (MULTI && g > 0) nxA.load(P, a.T, I0, 0);
         for (int k0 = 0; k0 < kend; k0 += kGChunk) {
             __syncthreads();
-            nxB.store(sPB, sQB);
-            if (MULTI && g > 0) nxA.store(sPA, sQA);
+            nxB.template store<true>(sPB, sQB, s_sqP, s_sqQ);
+            if (MULTI && g > 0) nxA.template store<false>(sPA, sQA, nullptr, nullptr);
             __syncthreads();
             if (k0 + kGChunk < kend) {
                 nxB.load(P, a.T, I0 + 16 * kGramJ * g, k0 + kGChunk);
@@ -484,20 +512,15 @@ profile_gram_kernel(ProfileArgs a) {
             }
             if (I < a.T && k0 + kGChunk - 1 < I) {
                 // every column of the chunk lies left of the tile's first row:
-                // L is 1 for all (i, k), so the prefix norms take plain sums
-                // of squares of the B rows (this lane: the quad of columns
-                // 4 quarter .. + 3, as hi + lo)
+                // L is 1 for all (i, k), so the prefix norms add the B rows'
+                // sums of squares over the chunk, taken at staging (the lanes
+                // of quarter 0 add them; the quarters are summed at the end)
                 gram_chunk();
+                if (quarter == 0) {
 #pragma unroll
-                for (int c = 0; c < kGramJ; ++c) {
-                    const int bo = (16 * (wave + c) + col) * kGRow + 16 * quarter;
-                    const u32x4 pb = *reinterpret_cast<const u32x4*>(sPB + bo);
-                    const u32x4 qb = *reinterpret_cast<const u32x4*>(sQB + bo);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float xp = quad_value(pb, e), xq = quad_value(qb, e);
-                        sb[c] = fmaf(xp, xp, sb[c]);
-                        sc[c] = fmaf(xq, xq, sc[c]);
+                    for (int c = 0; c < kGramJ; ++c) {
+                        sb[c] += s_sqP[16 * (wave + c) + col];
+                        sc[c] += s_sqQ[16 * (wave + c) + col];
                     }
                 }
             } else if (I < a.T && k0 <= I + 15) {  // past I + 15 this wavefront's A rows are zero
