@@ -46,9 +46,15 @@ constexpr int kMaxWaves = 16;
 constexpr float kNegBig = -1.0e30f;
 // Pipeline depth in rows per thread group: 3 for one-wavefront workgroups
 // (large batches: many resident wavefronts per CU already keep HBM busy, and
-// the shallower pipeline frees registers), 4 otherwise.
+// the shallower pipeline frees registers).  Larger workgroups take 2 when the
+// launch alone brings kBigLaunchWaves wavefronts or more (8 per CU: enough
+// requests in flight, and deeper pipelines only lengthen the queues that the
+// later wavefronts wait in), else 4.  Measured on MI355X at 512 x 4, 256 x 8
+// (depth 2 faster) and 256 x 4, 128 x 8 wavefronts (depth 4 faster).
 constexpr int kRowsPerChunkOneWave = 3;
+constexpr int kRowsPerChunkBig = 2;
 constexpr int kRowsPerChunk = 4;
+constexpr long long kBigLaunchWaves = 2048;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -1069,8 +1075,10 @@ hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t
 
 template <typename F, int D>
 hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
-    return waves == 1 ? launch_decode_u<F, D, kRowsPerChunkOneWave>(mode, waves, a, s)
-                      : launch_decode_u<F, D, kRowsPerChunk>(mode, waves, a, s);
+    if (waves == 1) return launch_decode_u<F, D, kRowsPerChunkOneWave>(mode, waves, a, s);
+    if ((long long)a.lanes * a.splits * waves >= kBigLaunchWaves)
+        return launch_decode_u<F, D, kRowsPerChunkBig>(mode, waves, a, s);
+    return launch_decode_u<F, D, kRowsPerChunk>(mode, waves, a, s);
 }
 
 template <typename F, int D>

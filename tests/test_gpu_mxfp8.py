@@ -117,6 +117,15 @@ def test_sink4_and_head_dims(D):
     _parity(tiny(head_dim=D, sink=4, batch=3, heads=5))
 
 
+def test_big_launch_sampled_lanes():
+    """512 lanes x 4 wavefronts (the shallow row pipeline), sink-free and sink4."""
+    rng = np.random.default_rng(5)
+    for sink in (0, 4):
+        w = tiny(batch=32, heads=16, head_dim=128, sink=sink)
+        lanes = sorted({(0, 0), (31, 15)} | {(int(rng.integers(32)), int(rng.integers(16))) for _ in range(10)})
+        _parity(w, waves=4, lanes=lanes)
+
+
 @pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
 def test_every_workgroup_size(waves):
     _parity(tiny(head_dim=128), waves=waves)

@@ -176,6 +176,16 @@ def test_h2o_uniform_attention_on_gpu(N_att, r):
             assert sorted(tn - int(x) for x in offs[0][: cnt[0]]) == want, tn
 
 
+# ------------------------------------------------------------------ launches of 2048 wavefronts and more
+@pytest.mark.parametrize("policy", ALL)
+@pytest.mark.parametrize("dt", [synth.F32, synth.BF16, synth.MXFP8])
+def test_big_launches(policy, dt):
+    """512 lanes x 4 wavefronts: a launch the library runs with its shallow
+    row pipeline (depth 2); sampled lanes in lockstep with the oracle."""
+    w = tiny(batch=32, heads=16, head_dim=128, dtype=dt)
+    check_policy(policy, w, lanes=_sample_lanes(w, 12, 11), waves=4, read_every=9)
+
+
 # ------------------------------------------------------------------ the Janus-Pro-7B shape (one layer)
 def _sample_lanes(w, n, seed):
     rng = np.random.default_rng(seed)
