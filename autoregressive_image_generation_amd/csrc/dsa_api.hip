@@ -154,8 +154,9 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // Wavefronts per workgroup.  Measured on MI355X: the decode is fastest with
 // one to three thousand wavefronts per launch in total (one workgroup per
 // lane), so waves doubles while lanes * waves stays below 3072, every thread
-// group keeps at least the pipeline depth (4 rows) of work, and the workgroup
-// stays at 8 wavefronts or fewer (16 was slower at every measured shape).
+// group keeps at least its pipeline depth of rows (dsa::rows_in_flight) of
+// work, and the workgroup stays at 8 wavefronts or fewer (16 was slower at
+// every measured shape).
 int choose_waves(const dsa_state* st, long long rows, int splits = 1) {
     const int max_w = st->dtype == DSA_MXFP8 ? 8 : 16;  // MXFP8 workgroups stop at 8 wavefronts
     if (st->waves) return std::min(st->waves, max_w);
@@ -164,7 +165,7 @@ int choose_waves(const dsa_state* st, long long rows, int splits = 1) {
     const long long wgs = (long long)st->lanes * splits;  // workgroups per launch
     const long long per = (rows + splits - 1) / splits;   // rows per workgroup
     int w = 1;
-    while (w < 8 && wgs * (2 * w) < 3072 && per >= 4ll * gpw * (2 * w)) w *= 2;
+    while (w < 8 && wgs * (2 * w) < 3072 && per >= (long long)dsa::rows_in_flight(wgs, 2 * w) * gpw * (2 * w)) w *= 2;
     return w;
 }
 

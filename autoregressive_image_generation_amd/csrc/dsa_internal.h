@@ -102,6 +102,19 @@ struct ProfileArgs {
 };
 constexpr int kMaxProfileDist = 256;  // per-distance sums of a row tile live in LDS
 
+// Rows a thread group of a decode launch keeps in flight (the depth of its
+// row pipeline), by the launch's workgroups and wavefronts per workgroup: 3
+// for one-wavefront workgroups (large batches: many resident wavefronts per
+// CU already keep HBM busy, and the shallower pipeline frees registers); for
+// larger workgroups 2 when the launch alone brings 2048 wavefronts or more (8
+// per CU: enough requests in flight, and deeper pipelines only lengthen the
+// queues that the later wavefronts wait in), else 4.  Measured on MI355X at
+// 512 x 4 and 256 x 8 wavefronts (depth 2 faster) and at 256 x 4 and 128 x 8
+// (depth 4 faster).
+constexpr int rows_in_flight(long long workgroups, int waves) {
+    return waves == 1 ? 3 : workgroups * waves >= 2048 ? 2 : 4;
+}
+
 hipError_t launch_decode(int mode, int dtype, int D, int waves, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_profile(int dtype, int D, const ProfileArgs& a, hipStream_t s);
 // Device address, on the current device, of the library's static profile

@@ -44,17 +44,13 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 constexpr float kNegBig = -1.0e30f;
-// Pipeline depth in rows per thread group: 3 for one-wavefront workgroups
-// (large batches: many resident wavefronts per CU already keep HBM busy, and
-// the shallower pipeline frees registers).  Larger workgroups take 2 when the
-// launch alone brings kBigLaunchWaves wavefronts or more (8 per CU: enough
-// requests in flight, and deeper pipelines only lengthen the queues that the
-// later wavefronts wait in), else 4.  Measured on MI355X at 512 x 4, 256 x 8
-// (depth 2 faster) and 256 x 4, 128 x 8 wavefronts (depth 4 faster).
+// Pipeline depth in rows per thread group: rows_in_flight() (dsa_internal.h).
 constexpr int kRowsPerChunkOneWave = 3;
 constexpr int kRowsPerChunkBig = 2;
 constexpr int kRowsPerChunk = 4;
-constexpr long long kBigLaunchWaves = 2048;
+static_assert(rows_in_flight(1, 1) == kRowsPerChunkOneWave && rows_in_flight(512, 4) == kRowsPerChunkBig &&
+                  rows_in_flight(256, 4) == kRowsPerChunk,
+              "the launcher's depths are rows_in_flight()'s");
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -1075,10 +1071,14 @@ hipError_t launch_decode_u(int mode, int waves, const DecodeArgs& a, hipStream_t
 
 template <typename F, int D>
 hipError_t launch_decode_t(int mode, int waves, const DecodeArgs& a, hipStream_t s) {
-    if (waves == 1) return launch_decode_u<F, D, kRowsPerChunkOneWave>(mode, waves, a, s);
-    if ((long long)a.lanes * a.splits * waves >= kBigLaunchWaves)
-        return launch_decode_u<F, D, kRowsPerChunkBig>(mode, waves, a, s);
-    return launch_decode_u<F, D, kRowsPerChunk>(mode, waves, a, s);
+    switch (rows_in_flight((long long)a.lanes * a.splits, waves)) {
+        case kRowsPerChunkOneWave:
+            return launch_decode_u<F, D, kRowsPerChunkOneWave>(mode, waves, a, s);
+        case kRowsPerChunkBig:
+            return launch_decode_u<F, D, kRowsPerChunkBig>(mode, waves, a, s);
+        default:
+            return launch_decode_u<F, D, kRowsPerChunk>(mode, waves, a, s);
+    }
 }
 
 template <typename F, int D>

@@ -215,10 +215,6 @@ class Inputs:
 
 
 # ----------------------------------------------------------------------------- runs
-# Wavefronts per lane measured best on MI355X with two micro-batch streams
-# (full 30/32-layer loops; 0 = the library's own choice).
-MEASURED_WAVES = {"janus_pro_7b": 1, "janus_pro_1b": 4, "lumina_mgpt_7b_1024": 4, "hires_8100_sink4": 8}
-
 _STREAM_POOL = []
 
 
@@ -471,7 +467,7 @@ def library_waves(w, lanes, dtype=None):
     gpw = 64 // (w.head_dim // ept)
     rows = w.L_p + w.N_att
     wv = 1
-    while wv < 8 and lanes * 2 * wv < 3072 and rows >= 4 * gpw * 2 * wv:
+    while wv < 8 and lanes * 2 * wv < 3072 and rows >= (2 if lanes * 2 * wv >= 2048 else 4) * gpw * 2 * wv:
         wv *= 2
     return wv
 
@@ -700,7 +696,7 @@ def measure_workload(w, dev, args, headline):
     log("inputs ready in %.1f s" % inputs.gen_seconds)
     head_steps = w.batch * layers * w.heads * w.L_dec
     S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
-    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    waves = args.waves  # 0: the library's own choice
     steps, warmup = (args.steps, args.warmup) if headline else (args.leg_steps, 0)
     total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
     n_launch = w.L_dec * layers  # launches per stream
@@ -808,7 +804,7 @@ def headline_extras(w, inputs, res, dev, args):
 
     layers = args.layers or w.layers
     S = args.streams if args.streams > 0 else (2 if w.batch % 2 == 0 else 1)
-    waves = args.waves or (MEASURED_WAVES.get(w.name, 0) if S == 2 else 0)
+    waves = args.waves  # 0: the library's own choice
     head_steps = w.batch * layers * w.heads * w.L_dec
     sec = res["ms_per_step"] * 1e-3
     total_bytes = sum(sparse_bytes_per_head_step(w, t) for t in range(w.L_dec)) * w.batch * w.heads * layers
