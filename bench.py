@@ -52,6 +52,10 @@ TRAFFIC = {
     ("lumina_mgpt_7b_1024", 1): {"bytes_per_launch": 80.01e6, "algorithmic_bytes_per_launch": 79770624, "kernel_sha256_16": "43761a16b8c733fb"},
     # one stream, dispatches 192512-192811 (steps 6000-6009, phase 3); algorithmic bytes of the same launches 119491584 (phase 2 window: counters / algorithmic 1.0018)
     ("hires_8100_sink4", 1): {"bytes_per_launch": 119.7e6, "algorithmic_bytes_per_launch": 119491584, "kernel_sha256_16": "43761a16b8c733fb"},
+    # MXFP8 cache, two micro-batch streams (1536 lanes per launch), dispatches 24960-25259 of the
+    # Mx8 decode kernel (steps 400-404, phase 3); algorithmic bytes 39386112 (phase 2 window,
+    # steps 100-104: counters / algorithmic 1.0575)
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.81e6, "algorithmic_bytes_per_launch": 39386112, "kernel_sha256_16": "43761a16b8c733fb"},
 }
 
 LEG_WORKLOADS = "janus_pro_1b,lumina_mgpt_7b_1024,hires_8100_sink4"
@@ -885,6 +889,7 @@ def headline_extras(w, inputs, res, dev, args):
         res["mxfp8_kv"] = {"value": head_steps / s_m, "unit": "head-steps/s", "ms_per_step": s_m * 1e3,
                            "hbm_gbs": b / s_m / 1e9, "speedup_vs_bf16_kv": sec / s_m,
                            "traffic_per_launch": traffic_for(w.name + "_mxfp8", S),
+                           "traffic_over_algorithmic": traffic_for(w.name + "_mxfp8", S, ratio=True),
                            "algorithmic_bytes_per_launch": b / (w.L_dec * layers * S),
                            "byte_ratio": total_bytes / b, "workspace_gb": m.nbytes * S * layers / 1e9,
                            "kv": "MXFP8 (E4M3, E8M0 scale per 32), q/k/v bf16"}
