@@ -181,6 +181,55 @@ def _engineered_run(w, q, kp, vp, k, v):
     return out.cpu().numpy()[:, 0, 0, :d], trace[:, 0, 0, :], reads
 
 
+def _bf16_bits(x):
+    """bf16 bit patterns of values that bf16 holds exactly (the upper half of fp32)."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.array_equal(f.view(np.uint32) & 0xFFFF, np.zeros_like(f.view(np.uint32))), "not bf16-exact"
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("lanes,waves", [(1, 1), (512, 4)])
+@pytest.mark.parametrize("S", [0, 4])
+def test_tied_logits_bf16(lanes, waves, S):
+    """bf16 rows whose keys repeat three vectors, so the window's logits tie
+    exactly at most selection steps: every choice must be the oracle's (the
+    oldest of the lowest), with no near-tie allowance, for one-wavefront lanes
+    (row pipeline of depth 3) and 512 x 4 wavefronts (depth 2)."""
+    rng = np.random.default_rng(7 + S)
+    T, D, L_p, N_r, N_att = 90, 128, 4, 24, 8
+    B, H = (1, 1) if lanes == 1 else (32, 16)
+    base = rng.integers(-4, 5, size=(3, D)) / 4.0          # quarters: exact in bf16
+    q = rng.integers(-4, 5, size=(T, B, H, D)) / 4.0
+    k = base[rng.integers(0, 3, size=(T, B, H))]
+    v = rng.integers(-8, 9, size=(T, B, H, D)) / 8.0
+    kp = rng.integers(-4, 5, size=(B, L_p, H, D)) / 4.0
+    vp = rng.integers(-8, 9, size=(B, L_p, H, D)) / 8.0
+
+    def dev(x):
+        return to_dev(_bf16_bits(x), DEV)
+
+    w = tiny(batch=B, heads=H, L_p=L_p, L_dec=T, N_r=N_r, N_att=N_att, sink=S, dtype=synth.BF16, head_dim=D)
+    ins = (dev(q), dev(k), dev(v), dev(kp), dev(vp))
+    say("tied logits bf16 lanes=%d waves=%d S=%d" % (lanes, waves, S))
+    out, trace, _ = run_sparse(w, ins, T, DEV, waves=waves)
+    out = out.cpu().numpy()
+    check = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(6 if lanes > 1 else 0)]
+    ties = 0
+    for b, h in check:
+        ref = oracle.run_lane(L_p, N_r, N_att, S, q[:, b, h], kp[b, :, h], vp[b, :, h], k[:, b, h], v[:, b, h],
+                              masks=True)
+        np.testing.assert_array_equal(trace[:, b, h, 0], ref["choice"])
+        np.testing.assert_array_equal(trace[:, b, h, 1], ref["evicted"])
+        for t in np.nonzero(ref["choice"] >= 0)[0]:  # the candidates' lowest logit shared by several
+            cand = [p for p in np.nonzero(ref["att_mask"][t])[0] if p >= S]
+            logits = k[cand, b, h] @ q[t, b, h]
+            ties += int(np.sum(logits == logits.min()) > 1)
+        err = float(np.abs(out[:, b, h, :] - ref["out"]).max())
+        assert err <= 2e-2, err
+    say("  lanes checked=%d selection steps with tied lowest logits=%d" % (len(check), ties))
+    assert ties > 0
+
+
 def test_worked_example_on_gpu():
     with open(os.path.join(GOLDEN, "worked_example_nr7_natt4.json")) as f:
         g = json.load(f)
