@@ -11,7 +11,8 @@
 // 16 (MXFP8), 8 (bf16) or 4 (fp32) elements of K and of V per thread; a
 // wavefront works on 64 / TPR rows at a time.  Each group keeps its own online-softmax
 // state (m, l, acc) over the rows it visits; groups merge through DPP /
-// shuffles inside the wavefront and through LDS across wavefronts.
+// shuffles inside the wavefront and through LDS across wavefronts (with
+// plain rows each wavefront normalises its own slice of the output).
 // Single-query decode does about one flop per byte of KV, so the kernel is
 // bound by HBM bandwidth; MFMA has no role.
 //
@@ -37,6 +38,8 @@
 //     arrive in bf16; the appended row is quantised in the launch that
 //     appends it, and every decode row the attention reads, the current
 //     token's included, is the quantised one.
+#include <type_traits>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -692,7 +695,8 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         }
     }
 
-    // Across wavefronts: through LDS, merged in wave order by wave 0.
+    // Across wavefronts: through LDS (MXFP8, H2O and split launches: merged in
+    // wave order by wave 0; otherwise by output slices, below).
     if (wl < TPR) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) s_acc[wave][sl * EPT + e] = acc[e];
@@ -705,6 +709,53 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         }
     }
     __syncthreads();
+
+    // Plain rows in a workgroup of several wavefronts: every wavefront
+    // normalises and stores its own D / nwaves output dimensions, each the
+    // sum over the wavefronts' partial states weighted by 2^(m_w - max m),
+    // divided by the same sum of the l_w.  All partial states are read at
+    // once (the wavefront count a constant of the instance), so the last
+    // lane of a launch does not wait for a merge chained through one
+    // wavefront.  Wave 0 then stores the appended row and takes the selection.
+    constexpr bool SLICED = !MX && !SPLIT && MODE != MODE_H2O;
+    const bool sliced = SLICED && nwaves > 1;
+    if constexpr (SLICED) {
+        auto slice_out = [&](auto nw) {
+            constexpr int NW = decltype(nw)::value;
+            constexpr int DPW = D / NW;
+            static_assert(DPW <= 64, "one dimension per thread");
+            float mw[NW], lw[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                mw[w] = s_m[w];
+                lw[w] = s_l[w];
+            }
+            if (wl < DPW) {
+                const int dim = wave * DPW + wl;
+                float ow[NW];
+#pragma unroll
+                for (int w = 0; w < NW; ++w) ow[w] = s_acc[w][dim];
+                float mx = mw[0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
+                float l = 0.0f, o = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float c = __builtin_amdgcn_exp2f(mw[w] - mx);
+                    l = fmaf(c, lw[w], l);
+                    o = fmaf(c, ow[w], o);
+                }
+                a.out[(size_t)lane * D + dim] = o / l;
+            }
+        };
+        switch (nwaves) {
+            case 2: slice_out(std::integral_constant<int, 2>{}); break;
+            case 4: slice_out(std::integral_constant<int, 4>{}); break;
+            case 8: slice_out(std::integral_constant<int, 8>{}); break;
+            case 16: slice_out(std::integral_constant<int, 16>{}); break;
+            default: break;
+        }
+    }
     if (wave != 0) return;
 
     // MXFP8: the current token's row, quantised above, enters after the merge
@@ -741,7 +792,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         self_s = group_sum<TPR>(part * (double)self_ks);
     }
 
-    if (wl < TPR) {
+    if (wl < TPR && !sliced) {
         for (int w = 1; w < nwaves; ++w) {
             float acc2[EPT];
 #pragma unroll
@@ -830,7 +881,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     // The output and the appended row are stored once no global load is left
     // (H2O: after its score update).
     auto store_results = [&]() {
-        if (wl < TPR) {
+        if (wl < TPR && !sliced) {
             const float inv = 1.0f / sm.l;
             float4* o4 = reinterpret_cast<float4*>(a.out + (size_t)lane * D + sl * EPT);
 #pragma unroll
@@ -843,7 +894,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
 
     if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
         if (wl != 0) return;
-        for (int w = 1; w < nwaves; ++w) {
+        for (int w = 1; w < (a.select ? nwaves : 1); ++w) {
             if (s_bd[w] >= 0 && (best_d < 0 || better(s_bs[w], s_bd[w], best_s, best_d))) {
                 best_s = s_bs[w];
                 best_d = s_bd[w];
