@@ -268,6 +268,20 @@ __device__ __forceinline__ bool better(double s, int d, double bs, int bd) {
     return s < bs || (s == bs && d > bd);
 }
 
+// Calls f with the workgroup's wavefront count (2, 4, 8 or 16) as a compile-time
+// constant, so that a loop over the wavefronts' partial states unrolls and
+// all of its LDS reads are issued at once.
+template <typename Fn>
+__device__ __forceinline__ void with_wave_count(int nwaves, Fn&& f) {
+    switch (nwaves) {
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 8: f(std::integral_constant<int, 8>{}); break;
+        case 16: f(std::integral_constant<int, 16>{}); break;
+        default: break;
+    }
+}
+
 // Wavefront-wide reductions of doubles (butterfly: every lane ends with the result).
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
@@ -748,13 +762,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
                 a.out[(size_t)lane * D + dim] = o / l;
             }
         };
-        switch (nwaves) {
-            case 2: slice_out(std::integral_constant<int, 2>{}); break;
-            case 4: slice_out(std::integral_constant<int, 4>{}); break;
-            case 8: slice_out(std::integral_constant<int, 8>{}); break;
-            case 16: slice_out(std::integral_constant<int, 16>{}); break;
-            default: break;
-        }
+        with_wave_count(nwaves, slice_out);
     }
     if (wave != 0) return;
 
@@ -793,12 +801,37 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     }
 
     if (wl < TPR && !sliced) {
-        for (int w = 1; w < nwaves; ++w) {
-            float acc2[EPT];
+        // wave 0's state and the others' from LDS, weighted by 2^(m_w - max m)
+        with_wave_count(nwaves, [&](auto nw) {
+            constexpr int NW = decltype(nw)::value;
+            float mw[NW], lw[NW];
+            mw[0] = sm.m;
+            lw[0] = sm.l;
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) acc2[e] = s_acc[w][sl * EPT + e];
-            merge<EPT>(sm, acc, s_m[w], s_l[w], acc2);
-        }
+            for (int w = 1; w < NW; ++w) {
+                mw[w] = s_m[w];
+                lw[w] = s_l[w];
+            }
+            float mx = mw[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
+            float cw[NW];
+            float l = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                cw[w] = __builtin_amdgcn_exp2f(mw[w] - mx);
+                l = fmaf(cw[w], lw[w], l);
+            }
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                float o = acc[e] * cw[0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) o = fmaf(cw[w], s_acc[w][sl * EPT + e], o);
+                acc[e] = o;
+            }
+            sm.m = mx;
+            sm.l = l;
+        });
         if constexpr (MX) {
             if (self_in) {
                 const float x = (float)(self_s * a.scale_log2e);
@@ -894,12 +927,27 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
 
     if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
         if (wl != 0) return;
-        for (int w = 1; w < (a.select ? nwaves : 1); ++w) {
-            if (s_bd[w] >= 0 && (best_d < 0 || better(s_bs[w], s_bd[w], best_s, best_d))) {
-                best_s = s_bs[w];
-                best_d = s_bd[w];
-                best_j = s_bj[w];
-            }
+        // the other wavefronts' candidates, in wave order (steps that select)
+        if (a.select) {
+            with_wave_count(nwaves, [&](auto nw) {
+                constexpr int NW = decltype(nw)::value;
+                double bs[NW];
+                int bd[NW], bj[NW];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    bs[w] = s_bs[w];
+                    bd[w] = s_bd[w];
+                    bj[w] = s_bj[w];
+                }
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    if (bd[w] >= 0 && (best_d < 0 || better(bs[w], bd[w], best_s, best_d))) {
+                        best_s = bs[w];
+                        best_d = bd[w];
+                        best_j = bj[w];
+                    }
+                }
+            });
         }
         if constexpr (MX) {
             // the current token as a candidate: offset 0
