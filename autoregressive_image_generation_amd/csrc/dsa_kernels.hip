@@ -800,49 +800,45 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
         self_s = group_sum<TPR>(part * (double)self_ks);
     }
 
-    if (wl < TPR && !sliced) {
-        // wave 0's state and the others' from LDS, weighted by 2^(m_w - max m)
-        with_wave_count(nwaves, [&](auto nw) {
-            constexpr int NW = decltype(nw)::value;
-            float mw[NW], lw[NW];
-            mw[0] = sm.m;
-            lw[0] = sm.l;
+    if constexpr (!SLICED) {
+        if (wl < TPR && nwaves > 1) {
+            // wave 0's state and the others' from LDS, weighted by 2^(m_w -
+            // max m): the maximum over all partial states at once, then the
+            // sums two wavefronts at a time
+            float mx = sm.m;
+            with_wave_count(nwaves, [&](auto nw) {
+                constexpr int NW = decltype(nw)::value;
+                float mw[NW];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                mw[w] = s_m[w];
-                lw[w] = s_l[w];
-            }
-            float mx = mw[0];
+                for (int w = 1; w < NW; ++w) mw[w] = s_m[w];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
-            float cw[NW];
-            float l = 0.0f;
+                for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
+            });
+            const float c0 = __builtin_amdgcn_exp2f(sm.m - mx);
+            float l = sm.l * c0;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                cw[w] = __builtin_amdgcn_exp2f(mw[w] - mx);
-                l = fmaf(cw[w], lw[w], l);
-            }
+            for (int e = 0; e < EPT; ++e) acc[e] *= c0;
+#pragma unroll 2
+            for (int w = 1; w < nwaves; ++w) {
+                const float c = __builtin_amdgcn_exp2f(s_m[w] - mx);
+                l = fmaf(c, s_l[w], l);
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                float o = acc[e] * cw[0];
-#pragma unroll
-                for (int w = 1; w < NW; ++w) o = fmaf(cw[w], s_acc[w][sl * EPT + e], o);
-                acc[e] = o;
+                for (int e = 0; e < EPT; ++e) acc[e] = fmaf(c, s_acc[w][sl * EPT + e], acc[e]);
             }
             sm.m = mx;
             sm.l = l;
-        });
-        if constexpr (MX) {
-            if (self_in) {
-                const float x = (float)(self_s * a.scale_log2e);
-                const float mn = fmaxf(sm.m, x);
-                const float c = __builtin_amdgcn_exp2f(sm.m - mn);
-                const float p = __builtin_amdgcn_exp2f(x - mn);
-                sm.l = sm.l * c + p;
+        }
+    }
+    if constexpr (MX) {
+        if (wl < TPR && self_in) {
+            const float x = (float)(self_s * a.scale_log2e);
+            const float mn = fmaxf(sm.m, x);
+            const float c = __builtin_amdgcn_exp2f(sm.m - mn);
+            const float p = __builtin_amdgcn_exp2f(x - mn);
+            sm.l = sm.l * c + p;
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + (p * self_vs) * self_vf[e];
-                sm.m = mn;
-            }
+            for (int e = 0; e < EPT; ++e) acc[e] = acc[e] * c + (p * self_vs) * self_vf[e];
+            sm.m = mn;
         }
     }
     if constexpr (SPLIT) {
@@ -926,29 +922,34 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     if constexpr (MODE != MODE_H2O) store_results();
 
     if constexpr (MODE == MODE_SPARSE || MODE == MODE_TOVA) {
-        if (wl != 0) return;
-        // the other wavefronts' candidates, in wave order (steps that select)
-        if (a.select) {
-            with_wave_count(nwaves, [&](auto nw) {
-                constexpr int NW = decltype(nw)::value;
-                double bs[NW];
-                int bd[NW], bj[NW];
-#pragma unroll
-                for (int w = 1; w < NW; ++w) {
-                    bs[w] = s_bs[w];
-                    bd[w] = s_bd[w];
-                    bj[w] = s_bj[w];
+        if (a.select && nwaves > 1) {
+            // Wavefront w's candidate in lane w of wave 0 (lane 0: its own),
+            // reduced over the first 16 lanes by rotations of 1, 2, 4 and 8
+            // (the candidate order is total, so the minimum is the same in
+            // any order of merging).
+            if (wl >= nwaves) best_d = -1;
+            if (wl >= 1 && wl < nwaves) {
+                best_s = s_bs[wl];
+                best_d = s_bd[wl];
+                best_j = s_bj[wl];
+            }
+            auto rotate = [&](auto cc) {
+                constexpr int CTRL = decltype(cc)::value;
+                const double bs2 = dpp_f64<CTRL>(best_s);
+                const int bd2 = __builtin_amdgcn_mov_dpp(best_d, CTRL, 0xF, 0xF, true);
+                const int bj2 = __builtin_amdgcn_mov_dpp(best_j, CTRL, 0xF, 0xF, true);
+                if (bd2 >= 0 && (best_d < 0 || better(bs2, bd2, best_s, best_d))) {
+                    best_s = bs2;
+                    best_d = bd2;
+                    best_j = bj2;
                 }
-#pragma unroll
-                for (int w = 1; w < NW; ++w) {
-                    if (bd[w] >= 0 && (best_d < 0 || better(bs[w], bd[w], best_s, best_d))) {
-                        best_s = bs[w];
-                        best_d = bd[w];
-                        best_j = bj[w];
-                    }
-                }
-            });
+            };
+            rotate(std::integral_constant<int, 0x121>{});  // row_ror:1
+            rotate(std::integral_constant<int, 0x122>{});  // row_ror:2
+            rotate(std::integral_constant<int, 0x124>{});  // row_ror:4
+            rotate(std::integral_constant<int, 0x128>{});  // row_ror:8
         }
+        if (wl != 0) return;
         if constexpr (MX) {
             // the current token as a candidate: offset 0
             if (self_in && a.select && (best_d < 0 || better(self_s, 0, best_s, best_d))) {
