@@ -274,11 +274,15 @@ def test_monotone_scores_on_gpu(direction, S):
 
 # ------------------------------------------------------------ dense kernel
 @pytest.mark.parametrize("dt,D", [(synth.F32, 64), (synth.BF16, 128)])
-def test_dense_matches_oracle(dt, D):
+@pytest.mark.parametrize("waves", [0, 2, 16])
+def test_dense_matches_oracle(dt, D, waves):
+    """waves 0: the library's choice; 2 and 16: the wavefronts of a lane
+    store their output slices from every partial state (D / 2 down to D / 16
+    dimensions each)."""
     w = tiny(dtype=dt, head_dim=D, batch=2)
     T = w.L_dec
     ins = device_inputs(w, 0, T, DEV)
-    out = run_dense(w, ins, T, DEV).cpu().numpy()
+    out = run_dense(w, ins, T, DEV, waves=waves).cpu().numpy()
     for b in range(w.batch):
         for h in range(w.heads):
             li = lane_inputs_from(w, 0, b, h, T)
