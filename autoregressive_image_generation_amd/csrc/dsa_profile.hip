@@ -70,19 +70,15 @@ struct MfmaIn<float> {  // fp32: 4 dimensions per step, 1 per lane
     __device__ static f32x4 mfma(Op a, Op b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
 };
 
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // Each wavefront of a workgroup takes 16 consecutive queries (kMapWaves x 16
 // per workgroup); keys are staged in LDS kMapKeys at a time, once per
 // workgroup (coalesced 16-byte loads), and read by every wavefront as
 // 16-key MFMA tiles; the next stage is loaded into registers while the
 // current one is consumed.  Lane l supplies tile row / column l % 16 and
-// dimensions by l / 16 of each MFMA step; it receives S[4 (l / 16) + e][l %
-// 16], e = 0..3.
+// dimensions by l / 16 of each MFMA step.  The tile is computed as K Q^T
+// (keys the A operand), so lane l receives the logits of query l % 16 with
+// the four consecutive keys 4 (l / 16) + e, e = 0..3: one 16-byte store of
+// the row's weights per lane and tile.
 constexpr int kMapWaves = 4;
 constexpr int kMapKeys = 64;  // keys per LDS stage: four 16-key tiles
 
@@ -123,14 +119,15 @@ struct KeyStage {
     }
 };
 
-// Logits of a wavefront's 16 queries (operand qa) against a staged 16-key
-// tile; krow: this lane's key row and dimension offset in LDS.
+// Logits of a staged 16-key tile against a wavefront's 16 queries (operand
+// qa), keys as the rows of the product; krow: this lane's key row and
+// dimension offset in LDS.
 template <typename T, int D>
 __device__ __forceinline__ f32x4 map_tile(const T* krow, const typename MfmaIn<T>::Op (&qa)[D / MfmaIn<T>::STEP]) {
     using M = MfmaIn<T>;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < D / M::STEP; ++s) acc = M::mfma(qa[s], M::load(krow + s * M::STEP), acc);
+    for (int s = 0; s < D / M::STEP; ++s) acc = M::mfma(M::load(krow + s * M::STEP), qa[s], acc);
     return acc;
 }
 
@@ -174,11 +171,12 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
     const int first_key = i0 + 15 < a.T ? min(a.L_p + i0, ncols - 1) : -1;
     const int last_key = a.L_p + min(i0 + 15, a.T - 1);
 
-    // pass 1: the maximum logit of each query over its columns (this lane's,
-    // then the 16 lanes of the query merged)
-    float m[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m[e] = -INFINITY;
+    // this lane's query, and its keys c = cmin + 4 quarter + e of each tile
+    const int i = i0 + col;
+
+    // pass 1: the maximum logit of this lane's query over its columns (this
+    // lane's four keys per tile, then the four lanes of the query merged)
+    float m = -INFINITY;
     pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
     for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
         __syncthreads();
@@ -197,33 +195,44 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
             for (int q2 = 0; q2 < 2; ++q2) {
                 const int cmin = c0 + 16 * (tp + q2);
                 if (cmin >= ncols || cmin > last_key) break;
-                const int c = cmin + col;
+                const int c = cmin + 4 * quarter;
                 const f32x4 t = ts[q2];
                 if (cmin + 15 <= first_key) {  // every key causal for every query (uniform)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) m[e] = fmaxf(m[e], t[e]);
+                    m = fmaxf(m, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = c < ncols && c <= a.L_p + i0 + 4 * quarter + e;
-                        m[e] = ok ? fmaxf(m[e], t[e]) : m[e];
+                        const bool ok = c + e < ncols && c + e <= a.L_p + i;
+                        m = ok ? fmaxf(m, t[e]) : m;
                     }
                 }
             }
         }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m[e] = fmaxf(m[e], __shfl_xor(m[e], o));
-        m[e] *= scale;  // scale > 0: the maximum of the scaled logits
-    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    m *= scale;  // scale > 0: the maximum of the scaled logits
 
     // pass 2: the weights 2^(x - m) of the decode keys (the probabilities up to
     // the row's normaliser: the cosines do not depend on a row's scale) and
     // the mass of each key group, divided by the row's total at the end
-    float* P = a.P + (size_t)lane * a.T * a.T;
-    float mp[4] = {0, 0, 0, 0}, ml[4] = {0, 0, 0, 0}, mm[4] = {0, 0, 0, 0};
+    float* const Prow = a.P + ((size_t)lane * a.T + min(i, a.T - 1)) * a.T;  // stored only for i < T
+    // 16-byte stores where every row and every decode quad starts 16-byte
+    // aligned (then no quad mixes prompt and decode keys), else per element
+    const bool vec = a.T % 4 == 0 && a.L_p % 4 == 0;
+    // the decode columns j0 .. j0 + 3 of this lane's query, up to the causal
+    // limit j <= i (and j < T)
+    auto store_quad = [&](int j0, float p0, float p1, float p2, float p3) {
+        if (vec && j0 >= 0 && j0 + 3 <= i) {
+            *reinterpret_cast<float4*>(Prow + j0) = make_float4(p0, p1, p2, p3);
+        } else {
+            const float pe[4] = {p0, p1, p2, p3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j0 + e >= 0 && j0 + e <= i && j0 + e < a.T) Prow[j0 + e] = pe[e];
+        }
+    };
+    float mp = 0.0f, ml = 0.0f, mm = 0.0f;
     pf.load(kp, k, a.L_p, a.B, a.H, b, h, ncols, 0);
     for (int c0 = 0; c0 < ncols; c0 += kMapKeys) {
         __syncthreads();
@@ -241,9 +250,9 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
             for (int q2 = 0; q2 < 2; ++q2) {
                 const int cmin = c0 + 16 * (tp + q2);
                 if (cmin >= ncols || cmin > last_key) break;
-                const int c = cmin + col;
+                const int c = cmin + 4 * quarter;
                 const f32x4 t = ts[q2];
-                const int j = c - a.L_p;  // decode position of the key
+                const int j0 = c - a.L_p;  // decode position of this lane's first key
                 // Uniform over the wavefront: every key of the tile causal for every
                 // query, and then all prompt keys, or all decode keys of every query's
                 // middle group (at most i - ceil((i + 1) / 10), which does not decrease
@@ -251,41 +260,45 @@ __global__ void __launch_bounds__(64 * kMapWaves) profile_map_kernel(ProfileArgs
                 const bool full = cmin + 15 <= first_key;
                 if (full && cmin + 15 < a.L_p) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mp[e] += __builtin_amdgcn_exp2f(t[e] * scale - m[e]);
+                    for (int e = 0; e < 4; ++e) mp += __builtin_amdgcn_exp2f(t[e] * scale - m);
                 } else if (full && cmin >= a.L_p && cmin + 15 - a.L_p <= i0 - (i0 + 10) / 10) {
+                    float p[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(t[e] * scale - m[e]);
-                        mm[e] += p;
-                        P[(size_t)(i0 + 4 * quarter + e) * a.T + j] = p;
+                        p[e] = __builtin_amdgcn_exp2f(t[e] * scale - m);
+                        mm += p[e];
                     }
+                    store_quad(j0, p[0], p[1], p[2], p[3]);
                 } else {
+                    const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
+                    float p[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int i = i0 + 4 * quarter + e;
-                        const bool ok = i < a.T && c < ncols && c <= a.L_p + i;
-                        const float p = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m[e]) : 0.0f;
-                        const int n_loc = (i + 10) / 10;  // local group: ceil((i + 1) / 10) most recent
-                        mp[e] += j < 0 ? p : 0.0f;
-                        ml[e] += j >= 0 && j > i - n_loc ? p : 0.0f;
-                        mm[e] += j >= 0 && j <= i - n_loc ? p : 0.0f;
-                        if (ok && j >= 0) P[(size_t)i * a.T + j] = p;
+                        const int j = j0 + e;
+                        const bool ok = i < a.T && c + e < ncols && j <= i;
+                        p[e] = ok ? __builtin_amdgcn_exp2f(t[e] * scale - m) : 0.0f;
+                        mp += j < 0 ? p[e] : 0.0f;
+                        ml += j >= 0 && j > i - n_loc ? p[e] : 0.0f;
+                        mm += j >= 0 && j <= i - n_loc ? p[e] : 0.0f;
                     }
+                    if (i < a.T && c < ncols) store_quad(j0, p[0], p[1], p[2], p[3]);
                 }
             }
         }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 4 * quarter + e;
-        const float vp = sum16(mp[e]), vl = sum16(ml[e]), vm = sum16(mm[e]);
-        if (col == 0 && i < a.T) {
-            const float inv = 1.0f / (vp + vl + vm);
-            float* r = a.mass_rows + ((size_t)lane * a.T + i) * 3;
-            r[0] = vp * inv;
-            r[1] = vl * inv;
-            r[2] = vm * inv;
-        }
+    // the query's sums over its four lanes
+    mp += __shfl_xor(mp, 16);
+    ml += __shfl_xor(ml, 16);
+    mm += __shfl_xor(mm, 16);
+    mp += __shfl_xor(mp, 32);
+    ml += __shfl_xor(ml, 32);
+    mm += __shfl_xor(mm, 32);
+    if (quarter == 0 && i < a.T) {
+        const float inv = 1.0f / (mp + ml + mm);
+        float* r = a.mass_rows + ((size_t)lane * a.T + i) * 3;
+        r[0] = mp * inv;
+        r[1] = ml * inv;
+        r[2] = mm * inv;
     }
 }
 
