@@ -156,7 +156,9 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // lane), so waves doubles while lanes * waves stays below 3072, every thread
 // group keeps at least its pipeline depth of rows (dsa::rows_in_flight) of
 // work, and the workgroup stays at 8 wavefronts or fewer (16 was slower at
-// every measured shape).
+// every measured shape).  Always 1, 2, 4, 8 or 16 (dsa_set_waves accepts no
+// other count): the kernel's merges across wavefronts are instantiated for
+// those counts only.
 int choose_waves(const dsa_state* st, long long rows, int splits = 1) {
     const int max_w = st->dtype == DSA_MXFP8 ? 8 : 16;  // MXFP8 workgroups stop at 8 wavefronts
     if (st->waves) return std::min(st->waves, max_w);
