@@ -17,8 +17,10 @@ enum Mode { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_TOVA = 2, MODE_H2O = 3 };
 // resolved here once and the kernel only sees its consequences.
 // Cache layout.  A row is K (D elements) then V (D elements).  Dense and
 // TOVA / H2O states: [lanes][lane_rows] rows (prompt rows, then decode rows or
-// slots).  Sparse states: the prompt region [lanes][L_p] rows at kv, then the
-// ring region at `ring`: [N_r][lanes] rows, i.e. ring index i (sinks 0..S-1,
+// slots).  Sparse states: the prompt region at kv, [lanes][L_p] rows or
+// [L_p][lanes] rows (prompt row j of every lane side by side; the prompt
+// strides below say which), then the ring region at `ring`: [N_r][lanes]
+// rows, i.e. ring index i (sinks 0..S-1,
 // then the window slots) of every lane side by side.  A step appends the same
 // ring index in every lane, so its writes form one contiguous block, and the
 // window reads of all lanes fall into the ring rows of a few indices.
@@ -38,6 +40,10 @@ struct DecodeArgs {
     char* scales;
     long long scale_rows;
     int lanes;
+    // sparse: bytes between a lane's prompt rows and between the lanes' first
+    // prompt rows (row bytes and L_p row bytes, or lanes row bytes and row
+    // bytes for a [L_p][lanes] prompt region)
+    long long prompt_row_bytes, prompt_lane_bytes;
     int L_p;
     int S;                 // sink count (0 or 4)
     int N_rw;              // ring length for non-sink entries: N_r - S
@@ -85,6 +91,7 @@ struct PromptArgs {
     int32_t* counter;      // nullable: when set, counter[lane] = 0 for every lane
     long long lane_rows;
     int B, H, L_p, list_stride;
+    int slot_major;        // sparse states: rows go to [L_p][lanes] instead of [lanes][lane_rows]
 };
 
 // Attention-map characterization (dsa_profile.hip).

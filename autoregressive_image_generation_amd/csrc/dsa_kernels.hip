@@ -347,7 +347,10 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     const int g = wave * GPW + wl / TPR;  // group index in the workgroup
     const int G = nwaves * GPW;
 
-    const char* lane_kv = reinterpret_cast<const char*>(a.kv) + (size_t)lane * (size_t)a.lane_rows * RB;
+    // sparse: this lane's first prompt row (prompt rows prompt_row_bytes apart);
+    // other modes: the lane's cache rows
+    const char* lane_kv = reinterpret_cast<const char*>(a.kv) +
+                          (size_t)lane * (MODE == MODE_SPARSE ? (size_t)a.prompt_lane_bytes : (size_t)a.lane_rows * RB);
     const char* ring = reinterpret_cast<const char*>(a.ring);
     const char* k_self = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k_new) + (size_t)lane * D);
     const char* v_self = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v_new) + (size_t)lane * D);
@@ -407,7 +410,7 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
             // the current token is a listed entry (offset 0) or, while t < S, a sink
             self = listed ? dl == 0 : (r >= a.L_p && r - a.L_p == a.t);
             const int ri = listed ? a.S + slot : max(r - a.L_p, 0);  // ring index of a sink or window entry
-            const char* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * RB;
+            const char* prow = lane_kv + (size_t)min(r, max(a.L_p - 1, 0)) * (size_t)a.prompt_row_bytes;
             const char* rrow = ring + ((size_t)ri * a.lanes + lane) * RB;
             row = r < a.L_p ? prow : rrow;
             sidx = r < a.L_p ? min(r, max(a.L_p - 1, 0)) : a.L_p + ri;
@@ -1049,9 +1052,10 @@ __global__ void __launch_bounds__(F::MX ? 512 : 1024) decode_kernel(DecodeArgs a
     }
 }
 
-// Prompt rows into the cache (plain: a copy; MXFP8: one block of 32 values
-// per thread, quantised), and the initial list entry {offset 0} of sink-free
-// sparse states.
+// Prompt rows into the cache ([lanes][lane_rows], or [L_p][lanes] for
+// slot-major sparse prompt regions; plain: a copy; MXFP8: one block of 32
+// values per thread, quantised), and the initial list entry {offset 0} of
+// sink-free sparse states.
 template <typename F, int D>
 __global__ void prompt_kernel(PromptArgs a) {
     using T = typename F::In;
@@ -1087,7 +1091,8 @@ __global__ void prompt_kernel(PromptArgs a) {
                 for (int e = 0; e < 4; ++e) w[q] |= e4m3_rne_sat(ldexpf(v[4 * q + e], -X)) << (8 * e);
             }
             const size_t lane = (size_t)b * a.H + h;
-            char* row = reinterpret_cast<char*>(a.kv) + (lane * (size_t)a.lane_rows + j) * RB;
+            const size_t ri = a.slot_major ? (size_t)j * ((size_t)a.B * a.H) + lane : lane * (size_t)a.lane_rows + j;
+            char* row = reinterpret_cast<char*>(a.kv) + ri * RB;
             uint4* dst = reinterpret_cast<uint4*>(row + half * D + blk * 32);
             dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
             dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -1110,8 +1115,8 @@ __global__ void prompt_kernel(PromptArgs a) {
             const char* src = reinterpret_cast<const char*>(half ? a.v_p : a.k_p) +
                               (((size_t)b * a.L_p + j) * a.H + h) * D * sizeof(T) + c * 16;
             const size_t lane = (size_t)b * a.H + h;
-            char* dst = reinterpret_cast<char*>(a.kv) + (lane * (size_t)a.lane_rows + j) * RB + half * D * sizeof(T) +
-                        c * 16;
+            const size_t ri = a.slot_major ? (size_t)j * ((size_t)a.B * a.H) + lane : lane * (size_t)a.lane_rows + j;
+            char* dst = reinterpret_cast<char*>(a.kv) + ri * RB + half * D * sizeof(T) + c * 16;
             *reinterpret_cast<uint4*>(dst) = load16(src);
         }
     }

@@ -101,6 +101,20 @@ def test_edge_cases(kw):
     _parity(tiny(**kw), read_every=3)
 
 
+@pytest.mark.parametrize("waves,sink", [(0, 0), (0, 4), (16, 0)])
+def test_slot_major_prompt_region(waves, sink):
+    """Sparse states of 1536 lanes and more keep the prompt region as [L_p][lanes]
+    rows (prompt position j of every lane side by side; written so by the
+    prompt copy and read so by the decode): a ragged prompt (L_p = 5) and
+    window, sampled lanes across the whole lane range in lockstep with the
+    oracle, also with sixteen wavefronts per lane and with sinks."""
+    w = tiny(dtype=synth.BF16, head_dim=128, batch=48, heads=32, L_p=5, N_r=16, N_att=6, L_dec=40, sink=sink)
+    rng = np.random.default_rng(7 + sink)
+    lanes = sorted({(int(x) // w.heads, int(x) % w.heads) for x in rng.integers(0, w.batch * w.heads, 10)})
+    lanes = sorted(set(lanes) | {(0, 0), (w.batch - 1, w.heads - 1)})
+    _parity(w, lanes=lanes, waves=waves)
+
+
 def test_largest_attended_list():
     """N_att - sink = DSA_MAX_ATTEND (8192 window offsets staged in LDS, 1024
     16-byte chunks loaded in the kernel's loop past the first two rounds):
