@@ -158,7 +158,7 @@ constexpr int kMaxH2oRows = DSA_MAX_H2O_ROWS;
 // prompt rows: with the rows of one prompt position side by side ([L_p][lanes])
 // those reads meet in fewer DRAM pages.  Measured on MI355X (full decodes, the
 // two layouts alternating, fraction of 8 TB/s): Janus-Pro-7B two streams (1536
-// lanes per launch) 0.845 against 0.823, one stream (3072) 0.707 / 0.706; with
+// lanes per launch) 0.843 against 0.821, one stream (3072) 0.702 / 0.704; with
 // fewer lanes and several wavefronts per lane, whose groups read many rows of
 // one lane at a time, [lanes][L_p] keeps them together: Lumina 1024^2 two
 // streams (256 lanes x 8 wavefronts) 0.739 against 0.715 slot-major.  MXFP8
