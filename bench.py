@@ -45,17 +45,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 # kernel source it was measured on: reported as null once that source changes.
 TRAFFIC = {
     # one stream, dispatches 12480-12779 (steps 400-409, phase 3); algorithmic bytes of the same launches 150386688 (phase 2 window: counters / algorithmic 1.0034)
-    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "algorithmic_bytes_per_launch": 150386688, "kernel_sha256_16": "b15310142fc0dbab"},
-    # one stream, dispatches 9984-10283 (steps 400-412, phase 3); algorithmic bytes of the same launches 32696320 (phase 2 window: counters / algorithmic 1.0057)
-    ("janus_pro_1b", 1): {"bytes_per_launch": 32.87e6, "algorithmic_bytes_per_launch": 32696320, "kernel_sha256_16": "b15310142fc0dbab"},
-    # one stream, dispatches 96512-96811 (steps 3000-3009, phase 3); algorithmic bytes of the same launches 79770624 (phase 2 window: counters / algorithmic 1.0034)
-    ("lumina_mgpt_7b_1024", 1): {"bytes_per_launch": 80.03e6, "algorithmic_bytes_per_launch": 79770624, "kernel_sha256_16": "b15310142fc0dbab"},
-    # one stream, dispatches 192512-192811 (steps 6000-6009, phase 3); algorithmic bytes of the same launches 119491584 (phase 2 window: counters / algorithmic 1.0019)
-    ("hires_8100_sink4", 1): {"bytes_per_launch": 119.7e6, "algorithmic_bytes_per_launch": 119491584, "kernel_sha256_16": "b15310142fc0dbab"},
+    ("janus_pro_7b", 1): {"bytes_per_launch": 150.8e6, "algorithmic_bytes_per_launch": 150386688, "kernel_sha256_16": "402cc1bfbc6d2ddc"},
+    # one stream, dispatches 9984-10283 (steps 400-412, phase 3); algorithmic bytes of the same launches 32696320 (phase 2 window: counters / algorithmic 1.0054)
+    ("janus_pro_1b", 1): {"bytes_per_launch": 32.86e6, "algorithmic_bytes_per_launch": 32696320, "kernel_sha256_16": "402cc1bfbc6d2ddc"},
+    # one stream, dispatches 96512-96811 (steps 3000-3009, phase 3); algorithmic bytes of the same launches 79770624 (phase 2 window: counters / algorithmic 1.0033)
+    ("lumina_mgpt_7b_1024", 1): {"bytes_per_launch": 80.01e6, "algorithmic_bytes_per_launch": 79770624, "kernel_sha256_16": "402cc1bfbc6d2ddc"},
+    # one stream, dispatches 192512-192811 (steps 6000-6009, phase 3); algorithmic bytes of the same launches 119491584 (phase 2 window: counters / algorithmic 1.0018)
+    ("hires_8100_sink4", 1): {"bytes_per_launch": 119.7e6, "algorithmic_bytes_per_launch": 119491584, "kernel_sha256_16": "402cc1bfbc6d2ddc"},
     # MXFP8 cache, two micro-batch streams (1536 lanes per launch), dispatches 24960-25259 of the
     # Mx8 decode kernel (steps 400-404, phase 3); algorithmic bytes 39386112 (phase 2 window,
     # steps 100-104: counters / algorithmic 1.0575)
-    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.80e6, "algorithmic_bytes_per_launch": 39386112, "kernel_sha256_16": "b15310142fc0dbab"},
+    ("janus_pro_7b_mxfp8", 2): {"bytes_per_launch": 42.83e6, "algorithmic_bytes_per_launch": 39386112, "kernel_sha256_16": "402cc1bfbc6d2ddc"},
 }
 
 LEG_WORKLOADS = "janus_pro_1b,lumina_mgpt_7b_1024,hires_8100_sink4"
