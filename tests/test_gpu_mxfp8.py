@@ -3,7 +3,8 @@
 * Bit-exact: every code and scale byte the library writes into the cache
   (prompt rows and appended rows) equals the oracle's quantisation of the same
   bf16 inputs; the workspace layout is the one the library documents (prompt
-  region [lanes][L_p] rows, ring region [N_r][lanes] rows, a row = K codes
+  region [lanes][L_p] rows at every lane count for MXFP8 states, ring region
+  [N_r][lanes] rows, a row = K codes
   then V codes; the rows' 8-byte scale words in a region of their own,
   [lanes][L_p + N_r] words).
 * Lockstep: choices and evictions exactly as the oracle run on the quantised
